@@ -1,1 +1,18 @@
-"""MI355X-native hot path of asynchronous block-diffusion speculative decoding."""
+"""MI355X-native hot path of asynchronous block-diffusion speculative decoding.
+
+The entry points live in the HIP library ``libd3d.so`` (C ABI in ``include/d3d.h``); the functions
+exported here are its thin Python binding with the same names. Build the library with
+``python -m block_diffusion_drafting_draft_amd.build``.
+"""
+
+_BOUND = ("d3d_build_branch_descs", "draft_attn_packed_workspace", "draft_attn_packed",
+          "spec_verify_workspace", "spec_verify", "branch_cache_match")
+
+__all__ = list(_BOUND)
+
+
+def __getattr__(name):
+    if name in _BOUND:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,233 @@
+"""ctypes binding of libd3d.so: argument marshalling only.
+
+Every function here has the name of the C entry point it wraps and does nothing but check the
+tensors it is handed, allocate outputs with torch (device memory is plumbing), pass raw pointers and
+torch's current HIP stream, and raise on a negative status. All arithmetic happens in the HIP
+kernels. There is no fallback: without the built library every call raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libd3d.so")
+
+D3D_BF16, D3D_F32 = 0, 1
+BLOCK_CAUSAL = 1
+MAX_REQ = 64
+
+_c = ctypes
+_i32p = _c.POINTER(_c.c_int32)
+
+_SIGNATURES = {
+    "d3d_build_branch_descs": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int32, _i32p,
+                                           _c.c_void_p, _c.c_int, _c.POINTER(_c.c_int)]),
+    "draft_attn_packed_workspace": (_c.c_size_t, [_i32p, _i32p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                                  _c.c_int]),
+    "draft_attn_packed": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                     _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                     _c.c_void_p, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                     _c.c_int, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                     _c.c_void_p]),
+    "spec_verify_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
+    "spec_verify": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                               _c.c_int, _c.c_float, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
+                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                               _c.c_size_t, _c.c_void_p]),
+    "branch_cache_match": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p,
+                                      _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "d3d_status_string": (_c.c_char_p, [_c.c_int]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+def load():
+    """Load libd3d.so (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m block_diffusion_drafting_draft_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load().d3d_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: status {status} ({msg})")
+
+
+def _host_i32(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(_i32p)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return D3D_BF16
+    if t.dtype == torch.float32:
+        return D3D_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return t
+
+
+# ------------------------------------------------------------------------------------------------
+def d3d_build_branch_descs(block_size, coverage, fanout, prefix_len, cur_anchor, alt_anchors):
+    """Host descriptor builder -> int32 array [(C-1)F + 2, 4] of (prefix_len, rej_pos, anchor, flags)."""
+    alt, alt_p = _host_i32(alt_anchors)
+    cap = max(0, (coverage - 1) * fanout + 2)
+    out = np.zeros((max(cap, 1), 4), dtype=np.int32)
+    n = ctypes.c_int(0)
+    _check(load().d3d_build_branch_descs(block_size, coverage, fanout, prefix_len, int(cur_anchor), alt_p,
+                                         out.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)),
+           "d3d_build_branch_descs")
+    return out[:n.value]
+
+
+def draft_attn_packed_workspace(req_block_off, req_prefix_len, block_size, n_heads_q, n_heads_kv, head_dim):
+    off, off_p = _host_i32(req_block_off)
+    pre, pre_p = _host_i32(req_prefix_len)
+    return int(load().draft_attn_packed_workspace(off_p, pre_p, len(pre), block_size, n_heads_q, n_heads_kv,
+                                                  head_dim))
+
+
+def draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, req_prefix_len, block_size,
+                      scale=None, page_table=None, page_size=16, kv_stride=None, out=None, ws=None,
+                      stream=None):
+    """Packed draft attention. q [N_q, H_q, d]; k_new/v_new [N_q, H_kv, d]; k_cache/v_cache either
+    [n_req, kv_stride, H_kv, d] (page_table None) or [n_pages, page_size, H_kv, d]; descs: device int32
+    [n_blocks, 4]; req_block_off / req_prefix_len: host ints. Returns out [N_q, H_q, d]."""
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (descs, "descs")):
+        _dev(t, n)
+    dt = _dtype_code(q)
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("q, k_new, v_new must share a dtype")
+    n_q, hq, d = q.shape
+    hkv = k_new.shape[1]
+    off, off_p = _host_i32(req_block_off)
+    pre, pre_p = _host_i32(req_prefix_len)
+    n_req = len(pre)
+    if off.size != n_req + 1 or int(off[-1]) * block_size != n_q:
+        raise ValueError("req_block_off does not match the packed query count")
+    if descs.dtype != torch.int32 or descs.shape != (int(off[-1]), 4):
+        raise ValueError("descs must be int32 [n_blocks, 4]")
+    if k_new.shape != (n_q, hkv, d) or v_new.shape != (n_q, hkv, d):
+        raise ValueError("k_new / v_new shape mismatch")
+    has_prefix = bool(pre.max(initial=0) > 0)
+    if has_prefix:
+        _dev(k_cache, "k_cache")
+        _dev(v_cache, "v_cache")
+        if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or k_cache.shape != v_cache.shape:
+            raise TypeError("k_cache / v_cache must match q's dtype and each other")
+        if k_cache.shape[-2:] != (hkv, d):
+            raise ValueError("k_cache / v_cache trailing dims must be [H_kv, d]")
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        if page_table.dtype != torch.int32 or page_table.dim() != 2 or page_table.shape[0] != n_req:
+            raise ValueError("page_table must be int32 [n_req, max_pages]")
+        max_pages, num_pages = page_table.shape[1], (k_cache.shape[0] if has_prefix else 1)
+        if has_prefix and k_cache.shape[1] != page_size:
+            raise ValueError("k_cache page dimension does not match page_size")
+        stride = 0
+    else:
+        max_pages, num_pages = 0, 0
+        stride = (k_cache.shape[1] if has_prefix else 0) if kv_stride is None else kv_stride
+        if has_prefix and k_cache.shape[0] != n_req:
+            raise ValueError("contiguous caches must be [n_req, kv_stride, H_kv, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out")
+    need = draft_attn_packed_workspace(off, pre, block_size, hq, hkv, d)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    scale = d ** -0.5 if scale is None else scale
+    st = load().draft_attn_packed(dt, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                  _ptr(k_cache) if has_prefix else None, _ptr(v_cache) if has_prefix else None,
+                                  _ptr(page_table), page_size, max_pages, num_pages, stride,
+                                  _ptr(descs), off_p, pre_p, n_req, block_size, hq, hkv, d, float(scale),
+                                  _ptr(out), _ptr(ws) if need else None, need, _stream(stream))
+    _check(st, "draft_attn_packed")
+    return out
+
+
+def spec_verify_workspace(n_req, n_draft, vocab):
+    return int(load().spec_verify_workspace(n_req, n_draft, vocab))
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, round_, ws=None, out=None,
+                stream=None):
+    """Speculative-sampling verify. target_logits [n_req, B, V], draft_logits [n_req, B-1, V],
+    draft_tokens int32 [n_req, B-1]. Returns a dict of device tensors: n_accepted, next_token, alpha,
+    survival, tau, flags."""
+    _dev(target_logits, "target_logits")
+    _dev(draft_tokens, "draft_tokens")
+    dt = _dtype_code(target_logits)
+    n_req, b, vocab = target_logits.shape
+    nd = b - 1
+    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (n_req, nd):
+        raise ValueError("draft_tokens must be int32 [n_req, B-1]")
+    if float(temperature) != 0.0 or draft_logits is not None:
+        _dev(draft_logits, "draft_logits")
+        if draft_logits.dtype != target_logits.dtype or draft_logits.shape != (n_req, nd, vocab):
+            raise ValueError("draft_logits must match target_logits' dtype and be [n_req, B-1, V]")
+    dev = target_logits.device
+    if out is None:
+        out = dict(n_accepted=torch.empty(n_req, dtype=torch.int32, device=dev),
+                   next_token=torch.empty(n_req, dtype=torch.int32, device=dev),
+                   alpha=torch.empty(n_req, nd, dtype=torch.float32, device=dev),
+                   survival=torch.empty(n_req, nd, dtype=torch.float32, device=dev),
+                   tau=torch.empty(n_req, dtype=torch.float32, device=dev),
+                   flags=torch.empty(n_req, dtype=torch.int32, device=dev))
+    need = spec_verify_workspace(n_req, nd, vocab)
+    if need == 0:
+        raise ValueError("unsupported verify shape")
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().spec_verify(dt, _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), n_req, nd, vocab,
+                            float(temperature), int(seed) & (2**64 - 1), int(round_) & 0xFFFFFFFF,
+                            _ptr(out["n_accepted"]), _ptr(out["next_token"]), _ptr(out["alpha"]),
+                            _ptr(out["survival"]), _ptr(out["tau"]), _ptr(out["flags"]), _ptr(ws), need,
+                            _stream(stream))
+    _check(st, "spec_verify")
+    return out
+
+
+def branch_cache_match(descs, req_block_off, n_accepted, next_token, hit=None, stream=None):
+    """descs int32 [n_blocks, 4], req_block_off int32 [n_req+1], n_accepted / next_token int32 [n_req],
+    all on the GPU. Returns hit_branch int32 [n_req] (-1 = miss)."""
+    for t, n in ((descs, "descs"), (req_block_off, "req_block_off"), (n_accepted, "n_accepted"),
+                 (next_token, "next_token")):
+        _dev(t, n)
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    n_req = n_accepted.numel()
+    if hit is None:
+        hit = torch.empty(n_req, dtype=torch.int32, device=n_accepted.device)
+    st = load().branch_cache_match(_ptr(descs), descs.shape[0], _ptr(req_block_off), n_req, _ptr(n_accepted),
+                                   _ptr(next_token), _ptr(hit), _stream(stream))
+    _check(st, "branch_cache_match")
+    return hit

@@ -1,0 +1,76 @@
+// Internal definitions shared by the gfx950 kernels and their host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "d3d.h"
+
+namespace d3d {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies; workgroups round-robin across them
+
+// bf16 <-> f32 (bf16 is the upper half of an IEEE binary32 value).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float load_elem(const __bf16 *p) {
+  return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t *>(p)) << 16);
+}
+__device__ __forceinline__ float load_elem(const float *p) { return *p; }
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC'11, section 3): per round, words 0 and 2 are multiplied by the round constants; the high
+// halves are mixed with words 1 and 3 and the round key; the key advances by the Weyl constants.
+struct Philox4 {
+  uint32_t x[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi_a = __umulhi(kMulA, c0), lo_a = kMulA * c0;
+    const uint32_t hi_b = __umulhi(kMulB, c2), lo_b = kMulB * c2;
+    const uint32_t n0 = hi_b ^ c1 ^ k0, n2 = hi_a ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo_b;
+    c2 = n2;
+    c3 = lo_a;
+    k0 += kWeylA;
+    k1 += kWeylB;
+  }
+  Philox4 out;
+  out.x[0] = c0;
+  out.x[1] = c1;
+  out.x[2] = c2;
+  out.x[3] = c3;
+  return out;
+}
+
+// Uniform double on the 53-bit grid of [0, 1): top 27 bits of word 0, top 26 bits of word 1.
+__device__ __forceinline__ double philox_uniform(uint64_t seed, uint32_t pos, uint32_t req,
+                                                 uint32_t round, uint32_t purpose) {
+  const Philox4 r = philox4x32_10(pos, req, round, purpose, static_cast<uint32_t>(seed),
+                                  static_cast<uint32_t>(seed >> 32));
+  const double hi = static_cast<double>(r.x[0] >> 5);
+  const double lo = static_cast<double>(r.x[1] >> 6);
+  return (hi * 67108864.0 + lo) * 0x1.0p-53;
+}
+
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? D3D_OK : D3D_EHIP;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace d3d

@@ -1,0 +1,77 @@
+// Branch-cache match, descriptor builder and status strings.
+//
+// [D3D] 前置知识: 异步起草与缓存命中: after verification, a branch drafted during the previous
+// round is reused when the verified prefix equals its start. With the accepted slice a0, y_1..y_n
+// and the resampled or bonus token t, the branch of rejection position r with anchor a reproduces
+// that prefix exactly when r = n + 1 and a = t. The first such block in pack order is returned.
+#include <algorithm>
+
+#include "d3d_internal.h"
+
+namespace d3d {
+namespace {
+
+__global__ __launch_bounds__(64) void match_kernel(const d3d_block_desc *descs, int total_blocks,
+                                                   const int32_t *off, int n_req,
+                                                   const int32_t *n_acc, const int32_t *next,
+                                                   int32_t *hit) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_req) return;
+  const int b0 = min(max(off[i], 0), total_blocks);
+  const int b1 = min(max(off[i + 1], b0), total_blocks);
+  const int want_r = n_acc[i] + 1;
+  const int tok = next[i];
+  int found = -1;
+  for (int b = b0 + 1; b < b1; ++b) {
+    const d3d_block_desc d = descs[b];
+    if (d.rej_pos == want_r && d.anchor == tok) {
+      found = b - b0;
+      break;
+    }
+  }
+  hit[i] = found;
+}
+
+}  // namespace
+}  // namespace d3d
+
+extern "C" int branch_cache_match(const d3d_block_desc *descs, int total_blocks,
+                                  const int32_t *req_block_off, int n_req,
+                                  const int32_t *n_accepted, const int32_t *next_token,
+                                  int32_t *hit_branch, hipStream_t stream) {
+  if (!descs || !req_block_off || !n_accepted || !next_token || !hit_branch) return D3D_EINVAL;
+  if (n_req < 1 || total_blocks < 1) return D3D_EINVAL;
+  const int threads = 64;
+  d3d::match_kernel<<<(n_req + threads - 1) / threads, threads, 0, stream>>>(
+      descs, total_blocks, req_block_off, n_req, n_accepted, next_token, hit_branch);
+  return d3d::launch_status();
+}
+
+extern "C" int d3d_build_branch_descs(int block_size, int coverage, int fanout, int prefix_len,
+                                      int32_t cur_anchor, const int32_t *alt_anchors,
+                                      d3d_block_desc *out, int cap, int *n_out) {
+  if (block_size < 1 || block_size > 64 || coverage < 2 || coverage > block_size || fanout < 1 ||
+      prefix_len < 0 || !alt_anchors || !out || !n_out)
+    return D3D_EINVAL;
+  const long long n = static_cast<long long>(coverage - 1) * fanout + 2;
+  if (n > cap) return D3D_EINVAL;
+  int w = 0;
+  out[w++] = d3d_block_desc{prefix_len, 0, cur_anchor, static_cast<int32_t>(D3D_BLOCK_CAUSAL)};
+  for (int k = 1; k < coverage; ++k)
+    for (int f = 0; f < fanout; ++f)
+      out[w++] = d3d_block_desc{prefix_len, k, alt_anchors[(k - 1) * fanout + f], 0};
+  out[w++] = d3d_block_desc{prefix_len, block_size, alt_anchors[(coverage - 1) * fanout], 0};
+  *n_out = w;
+  return D3D_OK;
+}
+
+extern "C" const char *d3d_status_string(int status) {
+  switch (status) {
+    case D3D_OK: return "ok";
+    case D3D_EINVAL: return "invalid argument or shape";
+    case D3D_EUNSUPPORTED: return "unsupported configuration";
+    case D3D_EHIP: return "HIP launch error";
+    case D3D_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}

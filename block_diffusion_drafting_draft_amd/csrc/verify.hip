@@ -1,0 +1,664 @@
+// Speculative-sampling verification on gfx950.
+//
+// What is computed ([D3D] 前置知识: 投机解码; [DScout] 前置知识: 推测解码, 平均接受长度 MAT,
+// 接受加权损失 AWL 与推测采样接受规则): per request, alpha_j = min(1, P_j(y_j)/Q_j(y_j)) for every
+// draft, the first rejection against Philox uniforms, the residual max(0, P - Q) or bonus draw,
+// the prefix-survival products S(k) and tau = 1 + sum_k S(k).
+//
+// Design (HBM-bound: the whole vocabulary of every row is read once):
+//   1. stats   grid (chunk, row): one coalesced 16-byte-vector pass over a slice of one logit row:
+//              running max (and first argmax), sum of exp((z - max)/T) with fp32 exp2 per element
+//              and fp64 accumulation per thread. Partial (max, argmax, sum) per (row, chunk).
+//   2. decide  one wavefront per request: merges the row partials in fp64, forms alpha_j from
+//              fp64 scalars, draws the Philox uniforms, finds the first rejection, S(k), tau.
+//   3. lse     grid (chunk, request): fp64 sum of exp((z - max)/T) over the one or two rows the
+//              draw needs (target row j*, and draft row j* after a rejection).
+//   4. mass    grid (chunk, request): fp64 residual (or bonus) mass per chunk.
+//   5. pick    one workgroup per request: chunk-level prefix over the masses, then a workgroup
+//              scan inside the chunk that holds u'Z, returning the smallest token whose inclusive
+//              cumulative mass exceeds u'Z.
+// Nothing returns to the host; every pass is stream-ordered after the previous one.
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+
+#include "d3d_internal.h"
+
+namespace d3d {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kStatTargetBlocks = 2048;
+constexpr int kStatMinChunk = 1024;
+constexpr int kSampleTargetBlocks = 2048;
+constexpr int kSampleMinChunk = 256;
+constexpr int kMaxSampleChunks = 1024;
+constexpr double kNear = 1e-6;
+
+struct StatPartial {
+  float max;
+  int32_t arg;
+  double sum;  // sum of exp((z - max) / T) over the chunk
+};
+
+enum SampleMode : int32_t { kDone = 0, kResidual = 1, kBonus = 2 };
+
+struct SampleState {
+  int32_t mode;
+  int32_t tgt_row;  // global target row index (request * (n_draft + 1) + j)
+  int32_t drf_row;  // global draft row index (request * n_draft + j)
+  float max_p;
+  float max_q;
+  int32_t pad;
+  double u;
+};
+
+struct VerifyArgs {
+  const void *target;
+  const void *draft;
+  const int32_t *tokens;
+  int n_req, n_draft, vocab, n_tgt_rows;
+  int chunks, chunk_len;
+  int s_chunks, s_chunk_len;
+  float c_log2;    // log2(e) / T
+  double inv_t;    // 1 / T (fp64)
+  uint64_t seed;
+  uint32_t round;
+  int greedy;
+  int32_t *n_acc;
+  int32_t *next_token;
+  float *alpha;
+  float *survival;
+  float *tau;
+  uint32_t *flags;
+  StatPartial *stats;
+  SampleState *state;
+  double *lse_part;   // [n_req][s_chunks][2]
+  double *mass_part;  // [n_req][s_chunks]
+};
+
+// ------------------------------------------------------------------------------------------------
+// block reductions (256 threads = 4 wavefronts)
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float block_max(float v, float *sh) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  float r = sh[0];
+  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ double block_sum(double v, double *sh) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  double r = sh[0];
+  for (int i = 1; i < kWaves; ++i) r += sh[i];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int *sh) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  int r = sh[0];
+  for (int i = 1; i < kWaves; ++i) r = min(r, sh[i]);
+  __syncthreads();
+  return r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 1. stats
+// ------------------------------------------------------------------------------------------------
+template <bool GREEDY>
+struct RowAcc {
+  float m = -INFINITY;
+  double s = 0.0;
+  int arg = INT_MAX;
+
+  // Fold 8 consecutive elements starting at token index `idx` (z in fp32, exact for bf16).
+  template <int N>
+  __device__ __forceinline__ void fold(const float (&z)[N], int idx, float c_log2, double inv_t) {
+    float vm = z[0];
+#pragma unroll
+    for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);
+    if constexpr (GREEDY) {
+      if (vm > m) {
+        m = vm;
+        int first = N - 1;
+#pragma unroll
+        for (int k = N - 1; k >= 0; --k)
+          if (z[k] == vm) first = k;
+        arg = idx + first;
+      }
+    } else {
+      if (vm > m) {
+        if (m != -INFINITY) s *= exp(static_cast<double>(m - vm) * inv_t);
+        m = vm;
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int k = 0; k < N; ++k) part += __builtin_amdgcn_exp2f((z[k] - m) * c_log2);
+      s += static_cast<double>(part);
+    }
+  }
+};
+
+__device__ __forceinline__ void unpack(const u32x4 &w, float (&z)[8], const __bf16 *) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    z[2 * k] = bf16_lo(w[k]);
+    z[2 * k + 1] = bf16_hi(w[k]);
+  }
+}
+__device__ __forceinline__ void unpack(const u32x4 &w, float (&z)[4], const float *) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) z[k] = __uint_as_float(w[k]);
+}
+
+template <typename T, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
+  __shared__ float sh_f[kWaves];
+  __shared__ double sh_d[kWaves];
+  __shared__ int sh_i[kWaves];
+  const int row = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const T *base = row < a.n_tgt_rows
+                      ? static_cast<const T *>(a.target) + static_cast<size_t>(row) * a.vocab
+                      : static_cast<const T *>(a.draft) +
+                            static_cast<size_t>(row - a.n_tgt_rows) * a.vocab;
+  const int begin = chunk * a.chunk_len;
+  const int end = min(begin + a.chunk_len, a.vocab);
+  RowAcc<GREEDY> acc;
+  if constexpr (VEC) {
+    constexpr int W = 16 / sizeof(T);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(base + begin);
+    const int nvec = (end - begin) / W;
+    constexpr int U = 4;
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += kThreads * U) {
+      u32x4 buf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kThreads;
+        if (v < nvec) buf[u] = vp[v];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kThreads;
+        if (v < nvec) {
+          float z[W];
+          unpack(buf[u], z, static_cast<const T *>(nullptr));
+          acc.fold(z, begin + v * W, a.c_log2, a.inv_t);
+        }
+      }
+    }
+  } else {
+    for (int idx = begin + threadIdx.x; idx < end; idx += kThreads) {
+      float z[1] = {load_elem(base + idx)};
+      acc.fold(z, idx, a.c_log2, a.inv_t);
+    }
+  }
+  const float m = block_max(acc.m, sh_f);
+  StatPartial out;
+  out.max = m;
+  if constexpr (GREEDY) {
+    out.arg = block_min_int(acc.m == m ? acc.arg : INT_MAX, sh_i);
+    out.sum = 0.0;
+  } else {
+    const double mine = acc.m == -INFINITY ? 0.0 : acc.s * exp(static_cast<double>(acc.m - m) * a.inv_t);
+    out.sum = block_sum(mine, sh_d);
+    out.arg = 0;
+  }
+  if (threadIdx.x == 0) a.stats[static_cast<size_t>(row) * a.chunks + chunk] = out;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 2. decide
+// ------------------------------------------------------------------------------------------------
+struct RowStat {
+  float max;
+  double sum;
+  int arg;
+};
+
+__device__ RowStat merge_row(const VerifyArgs &a, int row) {
+  const StatPartial *p = a.stats + static_cast<size_t>(row) * a.chunks;
+  float m = -INFINITY;
+  int arg = INT_MAX;
+  for (int c = 0; c < a.chunks; ++c) {
+    if (p[c].max > m) {
+      m = p[c].max;
+      arg = p[c].arg;
+    }
+  }
+  double s = 0.0;
+  if (!a.greedy)
+    for (int c = 0; c < a.chunks; ++c) s += p[c].sum * exp(static_cast<double>(p[c].max - m) * a.inv_t);
+  RowStat r;
+  r.max = m;
+  r.sum = s;
+  r.arg = arg;
+  return r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void decide_kernel(const VerifyArgs a) {
+  __shared__ double sh_alpha[64];
+  __shared__ double sh_u[64];
+  __shared__ int sh_arg[64];
+  __shared__ float sh_maxp[64];
+  __shared__ float sh_maxq[64];
+  __shared__ double sh_surv[64];
+  const int i = blockIdx.x;
+  const int j = threadIdx.x;
+  const int nd = a.n_draft;
+  const int V = a.vocab;
+  if (j <= nd) {
+    const RowStat rp = merge_row(a, i * (nd + 1) + j);
+    sh_arg[j] = rp.arg;
+    sh_maxp[j] = rp.max;
+    if (j < nd) {
+      const RowStat rq = a.greedy ? RowStat{0.f, 0.0, 0} : merge_row(a, a.n_tgt_rows + i * nd + j);
+      sh_maxq[j] = rq.max;
+      const int y = min(max(a.tokens[static_cast<size_t>(i) * nd + j], 0), V - 1);
+      double alpha;
+      if (a.greedy) {
+        alpha = (y == rp.arg) ? 1.0 : 0.0;
+      } else {
+        const T *zp = static_cast<const T *>(a.target) + (static_cast<size_t>(i) * (nd + 1) + j) * V;
+        const T *zq = static_cast<const T *>(a.draft) + (static_cast<size_t>(i) * nd + j) * V;
+        const double lp = (static_cast<double>(load_elem(zp + y)) - rp.max) * a.inv_t - log(rp.sum);
+        const double lq = (static_cast<double>(load_elem(zq + y)) - rq.max) * a.inv_t - log(rq.sum);
+        const double py = exp(lp), qy = exp(lq);
+        alpha = qy > 0.0 ? fmin(1.0, py / qy) : 1.0;
+      }
+      sh_alpha[j] = alpha;
+      sh_u[j] = philox_uniform(a.seed, static_cast<uint32_t>(j), static_cast<uint32_t>(i), a.round, 0u);
+    }
+  }
+  __syncthreads();
+  if (j == 0) {
+    int n_acc = nd;
+    uint32_t fl = 0;
+    double prod = 1.0, tau = 1.0;
+    for (int k = 0; k < nd; ++k) {
+      const double al = sh_alpha[k];
+      if (n_acc == nd) {
+        if (!a.greedy && fabs(sh_u[k] - al) < kNear) fl |= 1u;
+        if (!(sh_u[k] < al)) n_acc = k;
+      }
+      prod *= al;
+      sh_surv[k] = prod;
+      tau += prod;
+    }
+    a.n_acc[i] = n_acc;
+    if (a.tau) a.tau[i] = static_cast<float>(tau);
+    if (a.flags) a.flags[i] = fl;
+    SampleState st;
+    st.pad = 0;
+    st.tgt_row = i * (nd + 1) + n_acc;
+    st.drf_row = i * nd + min(n_acc, nd - 1);  // never read in bonus mode
+    st.max_p = sh_maxp[n_acc];
+    st.max_q = n_acc < nd ? sh_maxq[n_acc] : 0.f;
+    st.u = philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
+    if (a.greedy) {
+      st.mode = kDone;
+      a.next_token[i] = sh_arg[n_acc];
+    } else {
+      st.mode = n_acc < nd ? kResidual : kBonus;
+    }
+    a.state[i] = st;
+  }
+  __syncthreads();
+  if (j < nd) {
+    if (a.alpha) a.alpha[static_cast<size_t>(i) * nd + j] = static_cast<float>(sh_alpha[j]);
+    if (a.survival) a.survival[static_cast<size_t>(i) * nd + j] = static_cast<float>(sh_surv[j]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 3.-5. fp64 sample of the one row the next token is drawn from
+// ------------------------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ double centered(const T *row, int v, float mx, double inv_t) {
+  return (static_cast<double>(load_elem(row + v)) - static_cast<double>(mx)) * inv_t;
+}
+
+template <typename T>
+struct DrawRows {
+  const T *p;
+  const T *q;
+  float mp, mq;
+  double inv_t, log_sp, log_sq;
+  int mode;
+  // Mass of token v in the law being drawn from: max(0, P - Q) after a rejection, P for the bonus
+  // draw or the zero-mass fallback (mode != kResidual).
+  __device__ __forceinline__ double mass(int v) const {
+    const double ap = centered(p, v, mp, inv_t) - log_sp;
+    if (mode != kResidual) return exp(ap);
+    const double aq = centered(q, v, mq, inv_t) - log_sq;
+    if (!(ap > aq)) return 0.0;
+    return fmax(0.0, exp(ap) - exp(aq));
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sample_lse_kernel(const VerifyArgs a) {
+  __shared__ double sh_d[kWaves];
+  const int i = blockIdx.y;
+  const SampleState st = a.state[i];
+  if (st.mode == kDone) return;
+  const int V = a.vocab;
+  const T *p = static_cast<const T *>(a.target) + static_cast<size_t>(st.tgt_row) * V;
+  const T *q = static_cast<const T *>(a.draft) + static_cast<size_t>(st.drf_row) * V;
+  const int begin = blockIdx.x * a.s_chunk_len;
+  const int end = min(begin + a.s_chunk_len, V);
+  double sp = 0.0, sq = 0.0;
+  for (int v = begin + threadIdx.x; v < end; v += kThreads) {
+    sp += exp(centered(p, v, st.max_p, a.inv_t));
+    if (st.mode == kResidual) sq += exp(centered(q, v, st.max_q, a.inv_t));
+  }
+  sp = block_sum(sp, sh_d);
+  sq = block_sum(sq, sh_d);
+  if (threadIdx.x == 0) {
+    double *dst = a.lse_part + (static_cast<size_t>(i) * a.s_chunks + blockIdx.x) * 2;
+    dst[0] = sp;
+    dst[1] = sq;
+  }
+}
+
+template <typename T>
+__device__ DrawRows<T> draw_rows(const VerifyArgs &a, const SampleState &st, int i, double *sh_d) {
+  double sp = 0.0, sq = 0.0;
+  const double *src = a.lse_part + static_cast<size_t>(i) * a.s_chunks * 2;
+  for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
+    sp += src[2 * c];
+    sq += src[2 * c + 1];
+  }
+  sp = block_sum(sp, sh_d);
+  sq = block_sum(sq, sh_d);
+  DrawRows<T> d;
+  d.p = static_cast<const T *>(a.target) + static_cast<size_t>(st.tgt_row) * a.vocab;
+  d.q = static_cast<const T *>(a.draft) + static_cast<size_t>(st.drf_row) * a.vocab;
+  d.mp = st.max_p;
+  d.mq = st.max_q;
+  d.inv_t = a.inv_t;
+  d.log_sp = log(sp);
+  d.log_sq = st.mode == kResidual ? log(sq) : 0.0;
+  d.mode = st.mode;
+  return d;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sample_mass_kernel(const VerifyArgs a) {
+  __shared__ double sh_d[kWaves];
+  const int i = blockIdx.y;
+  const SampleState st = a.state[i];
+  if (st.mode == kDone) return;
+  const DrawRows<T> d = draw_rows<T>(a, st, i, sh_d);
+  const int begin = blockIdx.x * a.s_chunk_len;
+  const int end = min(begin + a.s_chunk_len, a.vocab);
+  double r = 0.0;
+  for (int v = begin + threadIdx.x; v < end; v += kThreads) r += d.mass(v);
+  r = block_sum(r, sh_d);
+  if (threadIdx.x == 0) a.mass_part[static_cast<size_t>(i) * a.s_chunks + blockIdx.x] = r;
+}
+
+// Inside [begin, end): the smallest v with offset + C(v) > target, where each thread owns one
+// contiguous run of tokens. Exactly one thread owns the crossing (its exclusive prefix and its
+// prefix plus its own mass bracket the target, both sums rounded identically); if rounding leaves
+// no crossing, the thread holding the last positive mass returns its last positive token.
+struct Found {
+  int v;
+  double c_v, c_prev;
+};
+
+template <typename T>
+__device__ Found scan_find(const DrawRows<T> &d, int begin, int end, double offset, double target,
+                           double *sh_pref) {
+  __shared__ Found sh_found;
+  __shared__ int sh_owner;
+  __shared__ int sh_last;
+  const int n = end - begin;
+  const int per = (n + kThreads - 1) / kThreads;
+  const int lo = begin + min(n, static_cast<int>(threadIdx.x) * per);
+  const int hi = begin + min(n, (static_cast<int>(threadIdx.x) + 1) * per);
+  double local = 0.0;
+  for (int v = lo; v < hi; ++v) local += d.mass(v);
+  sh_pref[threadIdx.x] = local;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double run = offset;
+    int owner = -1, last = -1;
+    for (int t = 0; t < kThreads; ++t) {
+      const double here = sh_pref[t];
+      const double next = run + here;
+      if (owner < 0 && run <= target && next > target) owner = t;
+      if (here > 0.0) last = t;
+      sh_pref[t] = run;  // exclusive prefix
+      run = next;
+    }
+    sh_owner = owner;
+    sh_last = last;
+    sh_found.v = -1;
+    sh_found.c_v = offset;
+    sh_found.c_prev = offset;
+  }
+  __syncthreads();
+  const int me = static_cast<int>(threadIdx.x);
+  const bool owner = me == sh_owner;
+  if (owner || (sh_owner < 0 && me == sh_last)) {
+    double c = sh_pref[me];
+    Found last{-1, c, c};
+    Found hit{-1, c, c};
+    for (int v = lo; v < hi; ++v) {
+      const double prev = c;
+      const double m = d.mass(v);
+      c += m;
+      if (m > 0.0) last = Found{v, c, prev};
+      if (owner && c > target) {
+        hit = Found{v, c, prev};
+        break;
+      }
+    }
+    sh_found = hit.v >= 0 ? hit : last;
+  }
+  __syncthreads();
+  const Found f = sh_found;
+  __syncthreads();
+  return f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs a) {
+  __shared__ double sh_d[kWaves];
+  __shared__ double sh_pref[kThreads];
+  __shared__ double sh_cum[kMaxSampleChunks];
+  __shared__ int sh_chunk;
+  const int i = blockIdx.x;
+  const SampleState st = a.state[i];
+  if (st.mode == kDone) return;
+  DrawRows<T> d = draw_rows<T>(a, st, i, sh_d);
+  const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
+  for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) sh_cum[c] = mass[c];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double run = 0.0;
+    for (int c = 0; c < a.s_chunks; ++c) {
+      run += sh_cum[c];
+      sh_cum[c] = run;  // inclusive
+    }
+  }
+  __syncthreads();
+  double z = sh_cum[a.s_chunks - 1];
+  uint32_t fl = 0;
+  Found f;
+  if (!(z > 0.0)) {
+    // zero residual mass (not reachable in exact arithmetic): draw from P instead
+    fl |= 4u;
+    d.mode = kBonus;
+    const double zp = [&] {
+      double s = 0.0;
+      for (int v = threadIdx.x; v < a.vocab; v += kThreads) s += d.mass(v);
+      return block_sum(s, sh_d);
+    }();
+    z = zp;
+    f = scan_find(d, 0, a.vocab, 0.0, st.u * z, sh_pref);
+  } else {
+    const double target = st.u * z;
+    if (threadIdx.x == 0) {
+      int c_star = -1, last_pos = -1;
+      double prev = 0.0;
+      for (int c = 0; c < a.s_chunks; ++c) {
+        if (sh_cum[c] > prev) last_pos = c;
+        if (c_star < 0 && sh_cum[c] > target) c_star = c;
+        prev = sh_cum[c];
+      }
+      sh_chunk = c_star >= 0 ? c_star : last_pos;
+    }
+    __syncthreads();
+    const int c = sh_chunk;
+    const double offset = c > 0 ? sh_cum[c - 1] : 0.0;
+    const int begin = c * a.s_chunk_len;
+    const int end = min(begin + a.s_chunk_len, a.vocab);
+    f = scan_find(d, begin, end, offset, target, sh_pref);
+  }
+  if (threadIdx.x == 0) {
+    const double target = st.u * z;
+    if (fabs(target - f.c_v) < kNear * z || fabs(target - f.c_prev) < kNear * z) fl |= 2u;
+    a.next_token[i] = f.v;
+    if (a.flags) a.flags[i] |= fl;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------------------------------
+struct VerifyPlan {
+  int chunks, chunk_len, s_chunks, s_chunk_len;
+  size_t off_stats, off_state, off_lse, off_mass, total;
+};
+
+int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
+  if (n_req < 1 || n_draft < 1 || n_draft > 63 || vocab < 1) return D3D_EINVAL;
+  const int rows = n_req * (2 * n_draft + 1);
+  int chunks = (kStatTargetBlocks + rows - 1) / rows;
+  chunks = std::max(1, std::min(chunks, (vocab + kStatMinChunk - 1) / kStatMinChunk));
+  int len = (vocab + chunks - 1) / chunks;
+  len = (len + 63) / 64 * 64;
+  p->chunk_len = len;
+  p->chunks = (vocab + len - 1) / len;
+  int s_chunks = (kSampleTargetBlocks + n_req - 1) / n_req;
+  s_chunks = std::max(1, std::min(s_chunks, (vocab + kSampleMinChunk - 1) / kSampleMinChunk));
+  int s_len = (vocab + s_chunks - 1) / s_chunks;
+  s_len = (s_len + 63) / 64 * 64;
+  s_chunks = (vocab + s_len - 1) / s_len;
+  if (s_chunks > kMaxSampleChunks) {
+    s_len = (vocab + kMaxSampleChunks - 1) / kMaxSampleChunks;
+    s_len = (s_len + 63) / 64 * 64;
+    s_chunks = (vocab + s_len - 1) / s_len;
+  }
+  p->s_chunk_len = s_len;
+  p->s_chunks = s_chunks;
+  size_t off = 0;
+  p->off_stats = off;
+  off = align_up(off + sizeof(StatPartial) * static_cast<size_t>(rows) * p->chunks, 256);
+  p->off_state = off;
+  off = align_up(off + sizeof(SampleState) * static_cast<size_t>(n_req), 256);
+  p->off_lse = off;
+  off = align_up(off + sizeof(double) * 2 * static_cast<size_t>(n_req) * s_chunks, 256);
+  p->off_mass = off;
+  off = align_up(off + sizeof(double) * static_cast<size_t>(n_req) * s_chunks, 256);
+  p->total = off;
+  return D3D_OK;
+}
+
+template <typename T>
+int launch_verify(const VerifyArgs &a, bool vec, hipStream_t stream) {
+  const dim3 stat_grid(a.chunks, a.n_req * (2 * a.n_draft + 1));
+  if (a.greedy) {
+    if (vec)
+      stats_kernel<T, true, true><<<stat_grid, kThreads, 0, stream>>>(a);
+    else
+      stats_kernel<T, false, true><<<stat_grid, kThreads, 0, stream>>>(a);
+  } else {
+    if (vec)
+      stats_kernel<T, true, false><<<stat_grid, kThreads, 0, stream>>>(a);
+    else
+      stats_kernel<T, false, false><<<stat_grid, kThreads, 0, stream>>>(a);
+  }
+  decide_kernel<T><<<a.n_req, 64, 0, stream>>>(a);
+  if (!a.greedy) {
+    const dim3 s_grid(a.s_chunks, a.n_req);
+    sample_lse_kernel<T><<<s_grid, kThreads, 0, stream>>>(a);
+    sample_mass_kernel<T><<<s_grid, kThreads, 0, stream>>>(a);
+    sample_pick_kernel<T><<<a.n_req, kThreads, 0, stream>>>(a);
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace d3d
+
+extern "C" size_t spec_verify_workspace(int n_req, int n_draft, int vocab) {
+  d3d::VerifyPlan p;
+  if (d3d::plan_verify(n_req, n_draft, vocab, &p) != D3D_OK) return 0;
+  return p.total;
+}
+
+extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                           const int32_t *draft_tokens, int n_req, int n_draft, int vocab,
+                           float temperature, uint64_t seed, uint32_t round, int32_t *n_accepted,
+                           int32_t *next_token, float *alpha, float *survival, float *tau,
+                           uint32_t *flags, void *ws, size_t ws_bytes, hipStream_t stream) {
+  using namespace d3d;
+  if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
+  if (!target_logits || !draft_tokens || !n_accepted || !next_token) return D3D_EINVAL;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return D3D_EINVAL;
+  const bool greedy = temperature == 0.f;
+  if (!greedy && !draft_logits) return D3D_EINVAL;
+  VerifyPlan p;
+  if (plan_verify(n_req, n_draft, vocab, &p) != D3D_OK) return D3D_EINVAL;
+  if (!ws || ws_bytes < p.total) return D3D_EWORKSPACE;
+  char *w = static_cast<char *>(ws);
+  VerifyArgs a;
+  a.target = target_logits;
+  a.draft = draft_logits;
+  a.tokens = draft_tokens;
+  a.n_req = n_req;
+  a.n_draft = n_draft;
+  a.vocab = vocab;
+  a.n_tgt_rows = n_req * (n_draft + 1);
+  a.chunks = p.chunks;
+  a.chunk_len = p.chunk_len;
+  a.s_chunks = p.s_chunks;
+  a.s_chunk_len = p.s_chunk_len;
+  a.c_log2 = greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  a.inv_t = greedy ? 0.0 : 1.0 / static_cast<double>(temperature);
+  a.seed = seed;
+  a.round = round;
+  a.greedy = greedy ? 1 : 0;
+  a.n_acc = n_accepted;
+  a.next_token = next_token;
+  a.alpha = alpha;
+  a.survival = survival;
+  a.tau = tau;
+  a.flags = flags;
+  a.stats = reinterpret_cast<StatPartial *>(w + p.off_stats);
+  a.state = reinterpret_cast<SampleState *>(w + p.off_state);
+  a.lse_part = reinterpret_cast<double *>(w + p.off_lse);
+  a.mass_part = reinterpret_cast<double *>(w + p.off_mass);
+  const size_t esize = dtype == D3D_BF16 ? 2 : 4;
+  const size_t width = 16 / esize;
+  const bool aligned = (reinterpret_cast<uintptr_t>(target_logits) % 16 == 0) &&
+                       (greedy || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
+  const bool vec = aligned && (static_cast<size_t>(vocab) % width == 0);
+  return dtype == D3D_BF16 ? launch_verify<__bf16>(a, vec, stream) : launch_verify<float>(a, vec, stream);
+}

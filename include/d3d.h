@@ -1,0 +1,180 @@
+/*
+ * d3d.h -- C ABI of the MI355X (gfx950) hot path of asynchronous block-diffusion speculative
+ * decoding: descriptor builder, packed draft attention, speculative-sampling verify, branch-cache
+ * match.
+ *
+ * Pages cited: [D3D] = the summary page "D3D: Decoupled Diffusion Drafting for Asynchronous
+ * Speculative Decoding"; [DScout] = the summary page "Factorization-Guided Training and Inference
+ * for Diffusion-Drafted Speculative Decoding". Sections are named by their headings.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller unless marked (host). The library never
+ *    allocates, frees or synchronises; GPU work is enqueued asynchronously on `stream`.
+ *  - Tensors are dense, row-major (last index fastest), with the element type given by `dtype`
+ *    (bf16 = IEEE bfloat16 bit patterns, f32 = IEEE binary32) unless stated otherwise.
+ *  - Return value: D3D_OK (0) or a negative status. Argument errors are found on the host before
+ *    anything is launched; d3d_status_string() describes a status. No C++ exception crosses the
+ *    ABI. The library holds no global mutable state and is thread-safe; two calls that share a
+ *    workspace must not overlap in time.
+ *  - Device-side contents (descriptors, page tables, token ids) are not validated on the host;
+ *    kernels clamp every index they derive from them so that no access leaves its buffer.
+ */
+#ifndef D3D_H
+#define D3D_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  D3D_OK = 0,
+  D3D_EINVAL = -1,       /* bad shape or argument; nothing launched */
+  D3D_EUNSUPPORTED = -2, /* valid but not implemented (head_dim, group size, ...) */
+  D3D_EHIP = -3,         /* a HIP launch reported an error */
+  D3D_EWORKSPACE = -4    /* workspace missing or smaller than the *_workspace() size */
+};
+
+typedef enum { D3D_BF16 = 0, D3D_F32 = 1 } d3d_dtype;
+
+/* flags bit of a block descriptor: the block is causal inside itself (else bidirectional). */
+#define D3D_BLOCK_CAUSAL 1u
+
+/* One packed block of B query rows: an anchor token followed by B-1 masked positions
+ * ([D3D] 方法步骤详情 step 2 and step 4; [DScout] 前置知识: 块扩散草稿器).
+ *  prefix_len : length of the request's shared, causally encoded prefix (informational).
+ *  rej_pos    : r, the number of rows of the request's first block (the current block) this block
+ *               also sees -- the accepted slice its branch assumes; 0 for the current block,
+ *               k for the branch of rejection position k, B for the full-accept branch.
+ *  anchor     : the anchor token id of the block.
+ *  flags      : D3D_BLOCK_CAUSAL or 0. */
+typedef struct {
+  int32_t prefix_len;
+  int32_t rej_pos;
+  int32_t anchor;
+  int32_t flags;
+} d3d_block_desc;
+
+/* ---------------------------------------------------------------------------------------------
+ * Descriptor builder (host only) -- [D3D] 方法步骤详情 step 4 and 技术新颖性: one packed forward
+ * pre-drafts, for each of the first C-1 rejection positions, F alternative anchors, plus the
+ * full-accept case: N_async = B[(C-1)F + 2] tokens.
+ *
+ * Writes (C-1)F + 2 descriptors to `out` (host), in pack order: the current block
+ * {prefix_len, 0, cur_anchor, CAUSAL}; then for k = 1..C-1 (major) and f = 0..F-1 the branch
+ * {prefix_len, k, alt_anchors[(k-1)F + f], 0}; then the full-accept block
+ * {prefix_len, B, alt_anchors[(C-1)F], 0}.
+ *  block_size B in [1, 64]; coverage C in [2, B]; fanout F >= 1; prefix_len >= 0.
+ *  alt_anchors (host): (C-1)F + 1 token ids.  cap: capacity of `out`.  n_out (host): count written.
+ * Errors: D3D_EINVAL on a bad argument or cap < (C-1)F + 2 (nothing written).
+ * ------------------------------------------------------------------------------------------- */
+int d3d_build_branch_descs(int block_size, int coverage, int fanout, int prefix_len,
+                           int32_t cur_anchor, const int32_t *alt_anchors,
+                           d3d_block_desc *out, int cap, int *n_out);
+
+/* ---------------------------------------------------------------------------------------------
+ * Packed draft attention -- one drafter attention layer of the packed forward ([D3D] 核心方法:
+ * prefix shared and causally encoded, attention bidirectional inside a block; 方法步骤详情 step 4).
+ *
+ * Requests are packed one after another. Request i owns blocks [req_block_off[i],
+ * req_block_off[i+1]) and query rows [B*req_block_off[i], B*req_block_off[i+1]); its first block
+ * is its current block. Query row t of block b (position j = t mod B) with query head h attends to
+ *   - every token of the request's prefix (req_prefix_len[i] tokens),
+ *   - rows [0, r_b) of the request's current block, when b is not the current block,
+ *   - the rows of its own block: all of them, or rows 0..j when the block is CAUSAL,
+ * with softmax(scale * q.k) weights over key/value head g = h / (n_heads_q / n_heads_kv).
+ *
+ *  q      [total_q, n_heads_q, head_dim]     total_q = B * req_block_off[n_req]
+ *  k_new, v_new [total_q, n_heads_kv, head_dim] the packed rows' own keys / values
+ *  k_cache, v_cache: prefix keys / values.
+ *     page_table == NULL: [n_req, kv_stride, n_heads_kv, head_dim]; request i's token p is at row
+ *                         i*kv_stride + p; needs req_prefix_len[i] <= kv_stride.
+ *     page_table != NULL: [num_pages, page_size, n_heads_kv, head_dim]; token p of request i is row
+ *                         p mod page_size of page page_table[i*max_pages + p/page_size]; needs
+ *                         req_prefix_len[i] <= max_pages*page_size. Page ids outside
+ *                         [0, num_pages) read as zero vectors.
+ *  descs  [total_blocks] device descriptors (rej_pos and flags are used; rej_pos is clamped to
+ *         [0, B]).
+ *  req_block_off (host) [n_req+1], non-decreasing, req_block_off[0] == 0.
+ *  req_prefix_len (host) [n_req], >= 0.
+ *  dtype  D3D_BF16 (fp32 accumulation, bf16 output) or D3D_F32 (fp32 throughout).
+ *  head_dim in {64, 128}; n_heads_q / n_heads_kv in {1, 2, 4, 8, 16}; 1 <= B <= 64;
+ *  1 <= n_req <= D3D_ATTN_MAX_REQ.
+ *  out    [total_q, n_heads_q, head_dim].
+ *  ws     workspace of at least draft_attn_packed_workspace(...) bytes (may be NULL if that is 0);
+ *         fp32 split-KV partial results; no initial contents are required.
+ * ------------------------------------------------------------------------------------------- */
+#define D3D_ATTN_MAX_REQ 64
+
+size_t draft_attn_packed_workspace(const int32_t *req_block_off, const int32_t *req_prefix_len,
+                                   int n_req, int block_size, int n_heads_q, int n_heads_kv,
+                                   int head_dim);
+
+int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_new, const void *v_new,
+                      const void *k_cache, const void *v_cache, const int32_t *page_table,
+                      int page_size, int max_pages, int num_pages, int kv_stride,
+                      const d3d_block_desc *descs, const int32_t *req_block_off,
+                      const int32_t *req_prefix_len, int n_req, int block_size, int n_heads_q,
+                      int n_heads_kv, int head_dim, float scale, void *out, void *ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Speculative-sampling verify ([D3D] 前置知识: 投机解码; [DScout] 前置知识: 推测解码, 平均接受长度
+ * MAT, 接受加权损失 AWL 与推测采样接受规则).
+ *
+ * For request i, target row j (j = 0..n_draft) and draft row j (j = 0..n_draft-1), with
+ * P_j = softmax(z^P_j / T) and Q_j = softmax(z^Q_j / T):
+ *   alpha_j = min(1, P_j(y_j) / Q_j(y_j))   (1 when Q_j(y_j) = 0)
+ *   u_j     = Philox4x32-10 uniform, key = seed, counter = (j, i, round, 0)
+ *   n_acc   = first j with u_j >= alpha_j, or n_draft when every draft is accepted
+ *   next    = residual draw from max(0, P_n_acc - Q_n_acc) (rejection) or from P_n_draft (bonus),
+ *             the smallest token v whose inclusive cumulative mass exceeds u' * Z, with
+ *             u' = Philox uniform, counter = (0, i, round, 1)
+ *   survival[k-1] = S(k) = prod_{j<k} alpha_j for k = 1..n_draft;  tau = 1 + sum_k S(k)
+ * Uniforms take the top 27 bits of output word 0 and the top 26 of word 1: a double on the
+ * 53-bit grid of [0, 1). temperature == 0 is greedy: alpha_j = [y_j == first argmax z^P_j], the
+ * next token is the first argmax of the target row; draft logits are not read.
+ * Precision: per-element exp in fp32 with fp64 accumulation for the acceptance statistics; the
+ * sampled row is recomputed entirely in fp64.
+ *
+ *  target_logits [n_req, n_draft+1, vocab], draft_logits [n_req, n_draft, vocab]  (dtype)
+ *  draft_tokens  [n_req, n_draft] int32 (ids outside [0, vocab) are clamped)
+ *  1 <= n_draft <= 63; vocab >= 1; temperature >= 0 and finite.
+ *  outputs: n_accepted [n_req] i32, next_token [n_req] i32, alpha [n_req, n_draft] f32,
+ *           survival [n_req, n_draft] f32, tau [n_req] f32, flags [n_req] u32:
+ *           bit0 some acceptance decision had |u_j - alpha_j| < 1e-6; bit1 the draw was within
+ *           1e-6 Z of a cumulative boundary; bit2 the residual mass was zero and the draw fell back
+ *           to P. Any output pointer except n_accepted and next_token may be NULL.
+ *  ws: at least spec_verify_workspace(...) bytes; no initial contents are required.
+ * ------------------------------------------------------------------------------------------- */
+size_t spec_verify_workspace(int n_req, int n_draft, int vocab);
+
+int spec_verify(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                const int32_t *draft_tokens, int n_req, int n_draft, int vocab, float temperature,
+                uint64_t seed, uint32_t round, int32_t *n_accepted, int32_t *next_token,
+                float *alpha, float *survival, float *tau, uint32_t *flags, void *ws,
+                size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Branch-cache match ([D3D] 前置知识: 异步起草与缓存命中): a verified outcome (n_acc accepted
+ * drafts, then token t) hits the branch whose assumed accepted slice and anchor it reproduces:
+ * the first block b after the request's current block, in pack order, with rej_pos == n_acc + 1
+ * and anchor == t. hit_branch[i] = b - req_block_off[i] (the block's index inside the request), or
+ * -1 on a miss. descs: [total_blocks]; req_block_off is a DEVICE array here, [n_req+1] (entries
+ * are clamped to [0, total_blocks]); n_accepted, next_token, hit_branch: [n_req]; n_req >= 1.
+ * ------------------------------------------------------------------------------------------- */
+int branch_cache_match(const d3d_block_desc *descs, int total_blocks, const int32_t *req_block_off,
+                       int n_req,
+                       const int32_t *n_accepted, const int32_t *next_token, int32_t *hit_branch,
+                       hipStream_t stream);
+
+const char *d3d_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* D3D_H */

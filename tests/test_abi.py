@@ -1,0 +1,99 @@
+"""The C-ABI library loads and exports every symbol include/d3d.h declares; host-side logic
+(descriptor builder, argument validation, workspace sizing) checked without a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_diffusion_drafting_draft_amd import _binding
+from oracle import packing
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "d3d.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"sizeof"})
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for want in ("d3d_build_branch_descs", "draft_attn_packed", "draft_attn_packed_workspace",
+                 "spec_verify", "spec_verify_workspace", "branch_cache_match", "d3d_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_binding.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_binding.EXPORTS) == set(_declared_functions())
+
+
+@pytest.mark.parametrize("B,C,F,L", [(16, 12, 2, 4096), (32, 16, 5, 8192), (4, 3, 1, 0), (8, 8, 3, 7)])
+def test_descriptor_builder_matches_oracle_packing(B, C, F, L):
+    rng = np.random.default_rng(B * 100 + C)
+    anchors = rng.integers(0, 151936, size=(C - 1) * F + 1)
+    a0 = int(rng.integers(0, 151936))
+    d = _binding.d3d_build_branch_descs(B, C, F, L, a0, anchors)
+    blocks = packing.pack_blocks(B, C, F, a0, anchors)
+    assert d.shape == (len(blocks), 4)
+    assert len(blocks) * B == packing.n_async(B, C, F)
+    for row, (r, anchor, causal) in zip(d, blocks):
+        assert tuple(int(x) for x in row) == (L, r, anchor, 1 if causal else 0)
+
+
+def test_descriptor_builder_rejects_bad_arguments():
+    with pytest.raises(RuntimeError, match="status -1"):
+        _binding.d3d_build_branch_descs(16, 17, 2, 0, 0, np.zeros(40))
+    with pytest.raises(RuntimeError, match="status -1"):
+        _binding.d3d_build_branch_descs(16, 1, 2, 0, 0, np.zeros(40))
+    with pytest.raises(RuntimeError, match="status -1"):
+        _binding.d3d_build_branch_descs(16, 12, 0, 0, 0, np.zeros(40))
+
+
+def test_status_strings():
+    lib = _binding.load()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.d3d_status_string(code)
+
+
+def test_host_validation_returns_before_launch():
+    """Bad shapes are rejected on the host (no device pointer is touched)."""
+    lib = _binding.load()
+    off = (ctypes.c_int32 * 2)(0, 24)
+    pre = (ctypes.c_int32 * 1)(4096)
+    fake = ctypes.c_void_p(256)
+    args = dict(page_table=None, page_size=16, max_pages=0, num_pages=0, kv_stride=4096)
+
+    def attn(hq=32, hkv=8, d=128, B=16, n_req=1, scale=0.088):
+        return lib.draft_attn_packed(0, fake, fake, fake, fake, fake, None, 16, 0, 0, 4096, fake, off, pre,
+                                     n_req, B, hq, hkv, d, scale, fake, None, 0, None)
+
+    assert attn(d=96) == -2           # head_dim not in {64, 128}
+    assert attn(hq=24, hkv=8) == -2   # group size 3
+    assert attn(hq=30, hkv=8) == -1   # not a multiple
+    assert attn(B=65) == -1
+    assert attn(n_req=0) == -1
+    assert attn(scale=0.0) == -1
+    assert attn() == -4               # the 8-way split needs a workspace
+    assert lib.spec_verify(0, fake, fake, fake, 1, 64, 100, 1.0, 0, 0, fake, fake, None, None, None, None,
+                           fake, 1 << 20, None) == -1
+    assert lib.spec_verify(0, fake, fake, fake, 1, 15, 100, -1.0, 0, 0, fake, fake, None, None, None, None,
+                           fake, 1 << 20, None) == -1
+    assert lib.spec_verify(0, fake, fake, fake, 1, 15, 100, 1.0, 0, 0, fake, fake, None, None, None, None,
+                           fake, 16, None) == -4
+    assert lib.branch_cache_match(fake, 0, fake, 1, fake, fake, fake, None) == -1
+
+
+def test_workspace_sizes():
+    # async pack, 384 queries, 4096-token prefix: 8 splits of 512 keys
+    assert _binding.draft_attn_packed_workspace([0, 24], [4096], 16, 32, 8, 128) == 8 * 384 * 32 * 130 * 4
+    # a serving batch of 16 requests has enough groups that no request is split
+    assert _binding.draft_attn_packed_workspace(list(range(0, 17 * 24, 24)), [4096] * 16, 16, 32, 8, 128) == 0
+    assert _binding.spec_verify_workspace(16, 15, 151936) > 0
+    assert _binding.spec_verify_workspace(1, 64, 10) == 0

@@ -1,0 +1,86 @@
+"""GPU parity of branch_cache_match and of one whole device round against the oracle."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_drafting_draft_amd import _binding, synth
+from gpu_util import AttnProblem, attn_close, dev, host, require_gpu
+from oracle import match as o_match
+from oracle import packing as o_pack
+from oracle import verify as o_ver
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _match(descs, off, n_acc, tok):
+    return _binding.branch_cache_match(
+        torch.from_numpy(np.ascontiguousarray(descs, np.int32)).cuda(),
+        torch.from_numpy(np.asarray(off, np.int32)).cuda(),
+        torch.from_numpy(np.asarray(n_acc, np.int32)).cuda(),
+        torch.from_numpy(np.asarray(tok, np.int32)).cuda()).cpu().numpy()
+
+
+def test_random_outcomes_match_oracle():
+    require_gpu()
+    _say("match: random outcomes, forced hits and misses")
+    rng = np.random.default_rng(1)
+    B, C, F = 16, 12, 2
+    descs, blocks, off = [], [], [0]
+    n_req = 200
+    for i in range(n_req):
+        anchors = rng.integers(0, 50, size=(C - 1) * F + 1)  # small id range: duplicates happen
+        descs.append(_binding.d3d_build_branch_descs(B, C, F, 100 + i, int(rng.integers(0, 50)), anchors))
+        blocks.append(o_pack.pack_blocks(B, C, F, 0, anchors))
+        off.append(off[-1] + len(blocks[-1]))
+    n_acc = rng.integers(0, B, size=n_req)
+    tok = rng.integers(0, 50, size=n_req)
+    # force hits on every 3rd request, misses (uncovered position) on every 7th
+    for i in range(0, n_req, 3):
+        b = int(rng.integers(1, len(blocks[i])))
+        n_acc[i], tok[i] = blocks[i][b][0] - 1, blocks[i][b][1]
+    for i in range(0, n_req, 7):
+        n_acc[i] = C  # rejection position C + 1 is not covered
+    got = _match(np.concatenate(descs), off, n_acc, tok)
+    want = np.array([o_match.match_request(blocks[i], int(n_acc[i]), int(tok[i])) for i in range(n_req)])
+    np.testing.assert_array_equal(got, want)
+    forced_hit = [i for i in range(0, n_req, 3) if i % 7]
+    assert (want[forced_hit] >= 0).all() and (want[::7] == -1).all()
+
+
+def test_one_device_round_async():
+    """Descriptor build -> packed attention -> verify -> match for the async workload, each against
+    the oracle; the match is fed the GPU verify outcome and compared with the oracle match of the
+    oracle outcome."""
+    require_gpu()
+    name = "async-B16C12F2-L4096-V151936"
+    _say(f"device round: {name}")
+    w = synth.WORKLOADS[name]
+    vin = synth.verify_inputs(w)
+    ain = synth.attention_inputs(w)
+    a0 = int(vin["cur_anchor"][0])
+    anchors = vin["alt_anchors"][0]
+    prob = AttnProblem("bf16", w.block_size,
+                       [dict(L=w.prefix[0], kind="async", C=w.coverage, F=w.fanout, a0=a0, anchors=anchors)], ain)
+    out = host(prob.run())
+    want, rows = prob.oracle()
+    ok, emax, fro = attn_close(out[rows], want, 2e-2, 1e-2)
+    _say(f"  attention max|err|={emax:.3g} rel_fro={fro:.3g}")
+    assert ok
+    res = _binding.spec_verify(dev(vin["z_target"], "bf16"), dev(vin["z_draft"], "bf16"),
+                               torch.from_numpy(vin["tokens"]).cuda(), 1.0, vin["philox_seed"], 0)
+    hit = _binding.branch_cache_match(prob.descs, torch.tensor(prob.off, dtype=torch.int32).cuda(),
+                                      res["n_accepted"], res["next_token"]).cpu().numpy()
+    o = o_ver.verify_request(vin["z_target"][0], vin["z_draft"][0], vin["tokens"][0], 1.0, vin["philox_seed"], 0, 0)
+    blocks = o_pack.pack_blocks(w.block_size, w.coverage, w.fanout, a0, anchors)
+    if not o.flags & 3:
+        assert int(res["n_accepted"][0]) == o.n_accepted and int(res["next_token"][0]) == o.next_token
+        assert int(hit[0]) == o_match.match_request(blocks, o.n_accepted, o.next_token)
+    _say(f"  n_acc={o.n_accepted} token={o.next_token} hit={int(hit[0])}")

@@ -1,0 +1,160 @@
+"""GPU parity of spec_verify against the oracle under shared Philox uniforms (through the C ABI).
+
+Bar: n_accepted and next_token bit-exact, except on draws the oracle flags as within 1e-6 of a
+threshold (counted and printed); |alpha - alpha_oracle| < 1e-6; tau within a relative 1e-5;
+survival within 1e-5 absolute."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+from scipy import special, stats
+
+from block_diffusion_drafting_draft_amd import _binding, synth
+from gpu_util import dev, require_gpu
+from oracle import verify as o_ver
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(zt, zd, tok, dtype, T, seed, round_):
+    t = dev(zt, dtype)
+    d = dev(zd, dtype) if zd is not None else None
+    y = torch.from_numpy(np.ascontiguousarray(tok, dtype=np.int32)).cuda()
+    out = _binding.spec_verify(t, d, y, T, seed, round_)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _compare(zt, zd, tok, T, seed, round_, got, name):
+    n_req = tok.shape[0]
+    flagged = mism = 0
+    for i in range(n_req):
+        o = o_ver.verify_request(zt[i], None if zd is None else zd[i], tok[i], T, seed, round_, i)
+        np.testing.assert_array_less(np.abs(got["alpha"][i] - o.alpha), 1e-6)
+        np.testing.assert_array_less(np.abs(got["survival"][i] - o.survival), 1e-5)
+        assert abs(got["tau"][i] - o.tau) <= 1e-5 * o.tau, (i, got["tau"][i], o.tau)
+        near_acc = bool(o.flags & o_ver.FLAG_NEAR_ACCEPT)
+        near_smp = bool(o.flags & o_ver.FLAG_NEAR_SAMPLE)
+        if near_acc or near_smp:
+            flagged += 1
+            if got["n_accepted"][i] != o.n_accepted or got["next_token"][i] != o.next_token:
+                mism += 1
+            continue
+        assert got["n_accepted"][i] == o.n_accepted, (name, i, got["n_accepted"][i], o.n_accepted)
+        assert got["next_token"][i] == o.next_token, (name, i, got["next_token"][i], o.next_token)
+        assert (got["flags"][i] & 4) == (o.flags & 4)
+    _say(f"  {name}: {n_req} requests, {flagged} oracle-flagged draws, {mism} of them differ")
+    return flagged
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity(name):
+    require_gpu()
+    w = synth.WORKLOADS[name]
+    _say(f"verify parity: {name}")
+    inp = synth.verify_inputs(w)
+    for round_ in range(3):
+        got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], w.dtype, inp["temperature"],
+                   inp["philox_seed"], round_)
+        _compare(inp["z_target"], inp["z_draft"], inp["tokens"], inp["temperature"], inp["philox_seed"],
+                 round_, got, f"{name} round {round_}")
+
+
+FUZZ = [
+    # dtype, n_req, B, V, T, logits
+    ("bf16", 3, 16, 1000, 1.0, "zipf"),
+    ("bf16", 2, 8, 1003, 0.7, "iid"),     # V not a multiple of 8: scalar path
+    ("f32", 4, 4, 64, 1.3, "iid"),
+    ("f32", 1, 2, 7, 1.0, "iid"),
+    ("bf16", 1, 32, 4096, 2.0, "zipf"),
+    ("bf16", 5, 24, 32000, 1.0, "zipf"),
+    ("f32", 3, 16, 1, 1.0, "iid"),        # one-token vocabulary: everything accepted
+    ("bf16", 2, 16, 151936, 0.0, "zipf"),  # greedy
+    ("f32", 6, 8, 50, 0.0, "iid"),        # greedy, small
+]
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=lambda c: "-".join(map(str, c)))
+def test_fuzz(case):
+    require_gpu()
+    dtype, n_req, B, V, T, kind = case
+    _say(f"verify fuzz: {case}")
+    base = synth.WORKLOADS["sync-bf16-L2048-V151936"]
+    w = synth.Workload("fuzz", dtype, 1, 1, 64, B, 0, 0, (0,), n_req, False, V, kind, 0.8, T,
+                       B * 1000 + V, 0xF00D + B)
+    inp = synth.verify_inputs(w)
+    if T == 0.0:
+        # make some drafts agree with the target argmax so greedy accepts a prefix
+        for i in range(n_req):
+            cut = (3 * i + 1) % B
+            inp["tokens"][i, :cut] = np.argmax(inp["z_target"][i, :cut], axis=-1)
+    got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], dtype, T, w.philox_seed, 5)
+    _compare(inp["z_target"], inp["z_draft"], inp["tokens"], T, w.philox_seed, 5, got, str(case))
+    del base
+
+
+def test_equal_distributions_accept_all_and_bonus_law():
+    """P = Q: every draft accepted (tau = B); over many requests the bonus follows P_{B-1}."""
+    require_gpu()
+    _say("verify: P = Q all-accept and bonus law")
+    rng = np.random.default_rng(5)
+    B, V, n_req = 4, 16, 8192
+    zp = synth.round_bf16(rng.normal(0, 1.0, size=(B, V)).astype(np.float32))
+    zt = np.broadcast_to(zp, (n_req, B, V)).copy()
+    zd = zt[:, :B - 1].copy()
+    tok = rng.integers(0, V, size=(n_req, B - 1)).astype(np.int32)
+    counts = np.zeros(V)
+    for round_ in range(4):
+        got = _run(zt, zd, tok, "bf16", 1.0, 77, round_)
+        assert np.all(got["n_accepted"] == B - 1)
+        assert np.all(got["alpha"] == 1.0)
+        np.testing.assert_allclose(got["tau"], B)
+        counts += np.bincount(got["next_token"], minlength=V)
+    p = special.softmax(zp[B - 1].astype(np.float64))
+    assert stats.chisquare(counts, p * counts.sum()).pvalue > 1e-3
+
+
+def test_first_emitted_token_follows_target():
+    """Losslessness on the GPU: with drafts drawn from Q, the first emitted token (the first draft
+    when accepted, else the residual draw) follows P_0."""
+    require_gpu()
+    _say("verify: first emitted token ~ P_0 over 2^17 draws")
+    rng = np.random.default_rng(6)
+    B, V, n_req = 4, 24, 16384
+    zp = synth.round_bf16(rng.normal(0, 1.2, size=(B, V)).astype(np.float32))
+    zq = synth.round_bf16((zp[:B - 1] + rng.normal(0, 1.0, size=(B - 1, V))).astype(np.float32))
+    zt = np.broadcast_to(zp, (n_req, B, V)).copy()
+    zd = np.broadcast_to(zq, (n_req, B - 1, V)).copy()
+    q = special.softmax(zq.astype(np.float64), axis=-1)
+    counts = np.zeros(V)
+    for round_ in range(8):
+        tok = np.stack([rng.choice(V, size=n_req, p=q[j]) for j in range(B - 1)], axis=1).astype(np.int32)
+        got = _run(zt, zd, tok, "bf16", 1.0, 0xABC, round_)
+        first = np.where(got["n_accepted"] >= 1, tok[:, 0], got["next_token"])
+        counts += np.bincount(first, minlength=V)
+        if round_ == 0:
+            _compare(zt[:64], zd[:64], tok[:64], 1.0, 0xABC, 0, {k: v[:64] for k, v in got.items()}, "law subset")
+    p = special.softmax(zp[0].astype(np.float64))
+    assert stats.chisquare(counts, p * counts.sum()).pvalue > 1e-3
+
+
+def test_residual_token_differs_from_rejected_draft():
+    require_gpu()
+    _say("verify: residual invariants")
+    w = synth.WORKLOADS["long-B32C16F5-L8192-V151936"]
+    inp = synth.verify_inputs(w, n_req=4, vocab=4096)
+    got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], "bf16", 1.0, 3, 0)
+    for i in range(4):
+        j = got["n_accepted"][i]
+        if j < 31:
+            assert got["next_token"][i] != inp["tokens"][i, j]
+            p = special.softmax(inp["z_target"][i, j].astype(np.float64))
+            q = special.softmax(inp["z_draft"][i, j].astype(np.float64))
+            assert p[got["next_token"][i]] > q[got["next_token"][i]]
