@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of one packed async draft round on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic round of the async workload
+(B = 16, C = 12, F = 2: 24 blocks, 384 packed queries; 32 query / 8 key-value heads, head dim 128,
+4096-token prefix; verify of 16 target + 15 draft rows over a 151936-token vocabulary):
+  1. branch descriptors built on the host and copied to the GPU from pinned memory,
+  2. draft_attn_packed (one drafter attention layer, all heads),
+  3. spec_verify (stats, decide, residual / bonus sample),
+  4. branch_cache_match.
+Inputs are resident in HBM before the timed region. The device part of a step (2-4) is captured
+once in a HIP graph; each step builds its descriptors on the host into a ring of pinned buffers,
+enqueues their copy and replays the graph. W untimed warm-up steps, then K timed steps between
+device synchronisations. Per-call durations come from HIP events recorded on the launch stream
+around K replays of a graph holding only that call. Prints one JSON line.
+
+`python bench.py --gpus N --steps K --warmup W [--workload NAME] [--no-cpu-baseline]`
+"""
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (2.5 PFLOP/s)
+MFMA_F32_PEAK_TFLOPS = 157.3
+METRIC = "µs per packed draft round (384 q) + attn TFLOP/s % MFMA peak; verify GB/s % HBM"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="async-B16C12F2-L4096-V151936")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle's timed CPU work")
+    return p.parse_args()
+
+
+def visible_pairs(B, blocks, L):
+    """(query, key) pairs one request's packed attention actually scores (the algorithmic work)."""
+    n = 0
+    for b, (r, causal) in enumerate(blocks):
+        for i in range(B):
+            n += L + (r if b > 0 else 0) + (i + 1 if causal else B)
+    return n
+
+
+class Round:
+    """Device-resident inputs of one round plus the calls of one step."""
+
+    def __init__(self, w):
+        import torch
+        from block_diffusion_drafting_draft_amd import _binding, synth
+        self.torch, self.lib, self.w = torch, _binding, w
+        _binding.load()
+        self.ain = synth.attention_inputs(w)
+        self.vin = synth.verify_inputs(w)
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        bits = (lambda x: torch.from_numpy(synth.f32_to_bf16_bits(x).view(np.int16).copy()).view(torch.bfloat16)) \
+            if w.dtype == "bf16" else (lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)))
+        cu = lambda x: bits(x).cuda()
+        self.B = w.block_size
+        self.lens = self.ain["prefix"]
+        self.n_req = len(self.lens)
+        self.q, self.k_new, self.v_new = cu(self.ain["q"]), cu(self.ain["k_new"]), cu(self.ain["v_new"])
+        if w.paged:
+            kp, table = synth.paginate(self.ain["k_prefix"], w.page_size, w.seed)
+            vp, _ = synth.paginate(self.ain["v_prefix"], w.page_size, w.seed)
+            self.k_cache, self.v_cache = cu(kp), cu(vp)
+            self.page_table = torch.from_numpy(table).cuda()
+        else:
+            stride = max(self.lens)
+            kc = np.zeros((self.n_req, stride) + self.ain["k_prefix"][0].shape[1:], np.float32)
+            vc = np.zeros_like(kc)
+            for i in range(self.n_req):
+                kc[i, :self.lens[i]] = self.ain["k_prefix"][i]
+                vc[i, :self.lens[i]] = self.ain["v_prefix"][i]
+            self.k_cache, self.v_cache = cu(kc), cu(vc)
+            self.page_table = None
+        self.z_t, self.z_d = cu(self.vin["z_target"]), cu(self.vin["z_draft"])
+        self.tokens = torch.from_numpy(self.vin["tokens"]).cuda()
+        # descriptors: host build each step into pinned memory, async copy to the device
+        self.blocks_per_req = [(w.coverage - 1) * w.fanout + 2 if w.coverage else 1] * self.n_req
+        self.off = np.concatenate([[0], np.cumsum(self.blocks_per_req)]).astype(np.int32)
+        n_blk = int(self.off[-1])
+        self.desc_host = torch.empty((n_blk, 4), dtype=torch.int32, pin_memory=True)
+        self.descs = torch.empty((n_blk, 4), dtype=torch.int32, device="cuda")
+        self.off_dev = torch.from_numpy(self.off).cuda()
+        self.out = torch.empty_like(self.q)
+        need = _binding.draft_attn_packed_workspace(self.off, self.lens, self.B, self.q.shape[1],
+                                                    self.k_new.shape[1], self.q.shape[2])
+        self.attn_ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        nd = self.B - 1
+        self.ver_ws = torch.empty(_binding.spec_verify_workspace(self.n_req, nd, w.vocab), dtype=torch.uint8,
+                                  device="cuda")
+        self.ver_out = dict(n_accepted=torch.empty(self.n_req, dtype=torch.int32, device="cuda"),
+                            next_token=torch.empty(self.n_req, dtype=torch.int32, device="cuda"),
+                            alpha=torch.empty(self.n_req, nd, dtype=torch.float32, device="cuda"),
+                            survival=torch.empty(self.n_req, nd, dtype=torch.float32, device="cuda"),
+                            tau=torch.empty(self.n_req, dtype=torch.float32, device="cuda"),
+                            flags=torch.empty(self.n_req, dtype=torch.int32, device="cuda"))
+        self.hit = torch.empty(self.n_req, dtype=torch.int32, device="cuda")
+        self.round = 0
+
+    def build_descs(self, pinned=None):
+        w = self.w
+        host = (self.desc_host if pinned is None else pinned).numpy()
+        for i in range(self.n_req):
+            a, b = self.off[i], self.off[i + 1]
+            if w.coverage:
+                host[a:b] = self.lib.d3d_build_branch_descs(self.B, w.coverage, w.fanout, self.lens[i],
+                                                            int(self.vin["cur_anchor"][i]), self.vin["alt_anchors"][i])
+            else:
+                host[a:b] = (self.lens[i], 0, int(self.vin["cur_anchor"][i]), 0)
+        if pinned is None:
+            self.descs.copy_(self.desc_host, non_blocking=True)
+
+    def attention(self):
+        self.lib.draft_attn_packed(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.descs,
+                                   self.off, self.lens, self.B, page_table=self.page_table,
+                                   page_size=self.w.page_size, out=self.out, ws=self.attn_ws)
+
+    def verify(self):
+        self.lib.spec_verify(self.z_t, self.z_d, self.tokens, self.vin["temperature"], self.vin["philox_seed"],
+                             self.round, ws=self.ver_ws, out=self.ver_out)
+        self.round += 1
+
+    def match(self):
+        self.lib.branch_cache_match(self.descs, self.off_dev, self.ver_out["n_accepted"],
+                                    self.ver_out["next_token"], hit=self.hit)
+
+    def work(self):
+        """Algorithmic FLOPs / bytes per call, counted from the pages' definitions."""
+        w = self.w
+        d, hq, hkv = self.q.shape[2], self.q.shape[1], self.k_new.shape[1]
+        es = 2 if w.dtype == "bf16" else 4
+        if w.coverage:
+            blocks = [(0, True)] + [(k, False) for k in range(1, w.coverage) for _ in range(w.fanout)] + \
+                     [(self.B, False)]
+        else:
+            blocks = [(0, False)]
+        pairs = sum(visible_pairs(self.B, blocks, L) for L in self.lens)
+        nq = self.q.shape[0]
+        attn_flops = 4 * d * hq * pairs
+        attn_bytes = es * (2 * nq * hq * d + 2 * nq * hkv * d + 2 * sum(self.lens) * hkv * d)
+        nd = self.B - 1
+        ver_bytes = es * self.n_req * (2 * nd + 1) * w.vocab + 4 * self.n_req * nd + \
+            self.n_req * (4 + 4 + 4 * nd + 4 * nd + 4 + 4)
+        return attn_flops, attn_bytes, ver_bytes
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, on the same round: packing + attention + verify + match, repeated
+    until `budget_s` seconds of CPU work; reports the median per round."""
+    from threadpoolctl import threadpool_info
+    from block_diffusion_drafting_draft_amd import synth
+    from oracle import attention, match, packing, verify
+    ain, vin = synth.attention_inputs(w), synth.verify_inputs(w)
+    B, d = w.block_size, ain["q"].shape[2]
+    nq = ain["q_per_req"][0]
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 50):
+        t0 = time.perf_counter()
+        for i, L in enumerate(ain["prefix"]):
+            if w.coverage:
+                blocks = packing.pack_blocks(B, w.coverage, w.fanout, int(vin["cur_anchor"][i]), vin["alt_anchors"][i])
+            else:
+                blocks = [(0, int(vin["cur_anchor"][i]), False)]
+            mask = packing.visible_mask(B, blocks, L)
+            sl = slice(i * nq, (i + 1) * nq)
+            attention.packed_attention(ain["q"][sl], ain["k_prefix"][i], ain["v_prefix"][i], ain["k_new"][sl],
+                                       ain["v_new"][sl], mask, d ** -0.5)
+            o = verify.verify_request(vin["z_target"][i], vin["z_draft"][i], vin["tokens"][i], vin["temperature"],
+                                      vin["philox_seed"], 0, i)
+            match.match_request(blocks, o.n_accepted, o.next_token)
+        times.append(time.perf_counter() - t0)
+    threads = max([p["num_threads"] for p in threadpool_info()] or [1])
+    return dict(value=statistics.median(times) * 1e6, unit="µs per packed draft round", cores=threads,
+                kind="oracle",
+                sample=f"{len(times)} full rounds of the same workload (all queries and heads, verify of every row, "
+                       f"match), float64 NumPy, median; not a tuned CPU implementation")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box here has a single GPU, so --gpus {args.gpus} is not run "
+              f"(the path shards by request or key/value head; see the design notes).", file=sys.stderr)
+        return 2
+    import torch
+    from block_diffusion_drafting_draft_amd import synth
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    w = synth.WORKLOADS[args.workload]
+    r = Round(w)
+    ring = [torch.empty_like(r.desc_host).pin_memory() for _ in range(3)]
+    copied = [torch.cuda.Event() for _ in ring]
+
+    def device_round():
+        r.attention()
+        r.verify()
+        r.match()
+
+    for _ in range(3):  # eager warm-up (first launches, code-object loads)
+        r.build_descs()
+        device_round()
+    torch.cuda.synchronize()
+    graphs = {}
+    for name, fn in (("round", device_round), ("draft_attn_packed", r.attention), ("spec_verify", r.verify),
+                     ("branch_cache_match", r.match)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+
+    def step(k):
+        slot = k % len(ring)
+        copied[slot].synchronize()          # the copy that last read this pinned slot has run
+        r.build_descs(ring[slot])
+        r.descs.copy_(ring[slot], non_blocking=True)
+        copied[slot].record(cur)
+        graphs["round"].replay()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    def call_us(name, reps):
+        g = graphs[name]
+        for _ in range(5):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(cur)
+        for _ in range(reps):
+            g.replay()
+        e1.record(cur)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    reps = max(args.steps, 20)
+    t_attn, t_ver, t_match = call_us("draft_attn_packed", reps), call_us("spec_verify", reps), \
+        call_us("branch_cache_match", reps)
+    t_round = call_us("round", reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(cur)
+    for k in range(reps):
+        r.descs.copy_(ring[k % len(ring)], non_blocking=True)
+    e1.record(cur)
+    e1.synchronize()
+    t_desc = e0.elapsed_time(e1) * 1e3 / reps
+    attn_flops, attn_bytes, ver_bytes = r.work()
+    peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    attn_tflops = attn_flops / (t_attn * 1e-6) / 1e12
+    ver_gbs = ver_bytes / (t_ver * 1e-6) / 1e9
+    traffic = None
+    tf = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as fh:
+            rec = json.load(fh)
+        if rec.get("workload") == w.name and rec.get("source_digest") == _kernel_digest():
+            traffic = rec.get("bytes_per_launch")
+    out = {
+        "metric": METRIC,
+        "value": round(ms_step * 1e3, 3),
+        "unit": "µs",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_req": r.n_req, "block_size": w.block_size, "coverage": w.coverage,
+                   "fanout": w.fanout, "prefix": r.lens if r.n_req > 1 else r.lens[0],
+                   "packed_queries": int(r.q.shape[0]), "heads_q": int(r.q.shape[1]),
+                   "heads_kv": int(r.k_new.shape[1]), "head_dim": int(r.q.shape[2]), "vocab": w.vocab,
+                   "paged": w.paged},
+        "calls_us": {"descriptor_copy": round(t_desc, 3), "draft_attn_packed": round(t_attn, 3),
+                     "spec_verify": round(t_ver, 3), "branch_cache_match": round(t_match, 3),
+                     "device_round": round(t_round, 3)},
+        "attn": {"tflops": round(attn_tflops, 2), "pct_mfma_peak": round(100 * attn_tflops / peak, 2),
+                 "flops": attn_flops, "bytes": attn_bytes},
+        "verify": {"gbs": round(ver_gbs, 1), "pct_hbm_peak": round(100 * ver_gbs / HBM_PEAK_GBS, 2),
+                   "bytes": ver_bytes},
+        "roofline": {"bound": "mfma", "kernel": "draft_attn_packed (attn_kernel + combine_kernel)",
+                     "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _kernel_digest():
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_diffusion_drafting_draft_amd", "csrc",
+                       "attn.hip")
+    with open(src, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -41,6 +41,7 @@ constexpr int kRows = 128;  // query-head rows per workgroup
 constexpr int kKeys = 64;   // keys per tile
 constexpr int kTargetItems = 768;
 constexpr int kMinSplit = 256;
+constexpr int kMaxSplits = 16;
 
 struct ReqInfo {
   int32_t q_begin;      // global packed row of the request's first query
@@ -104,57 +105,50 @@ __device__ __forceinline__ int vt_col(int kappa) {
   return (kappa & ~15) + 8 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
 }
 
-template <typename T>
-__device__ __forceinline__ const T *kv_row(const AttnArgs &a, const T *base, const ReqInfo &R,
-                                           int j, int g, int D, bool paged) {
-  if (!paged) return base + ((static_cast<size_t>(R.req) * a.kv_stride + j) * a.Hkv + g) * D;
-  const int page = a.page_table[static_cast<size_t>(R.req) * a.max_pages + j / a.page_size];
-  if (page < 0 || page >= a.num_pages) return nullptr;
-  return base + ((static_cast<size_t>(page) * a.page_size + (j % a.page_size)) * a.Hkv + g) * D;
-}
-
 template <typename T, int D>
 struct TileRegs {
   static constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
   static constexpr int NK = kKeys * CH / kThreads;                  // K chunks per thread
-  // bf16 V: (4-key group, 8-d group) pairs, f32 V: same as K
+  // bf16 V is loaded as (4-key group, 8-element d group) units, 4-key group index fastest so that
+  // the transposed LDS stores of a wavefront half hit distinct banks; f32 V is loaded like K.
   static constexpr int NVU = Cfg<T>::kBf16 ? (16 * (D / 8) + kThreads - 1) / kThreads : NK;
   u32x4 k[NK];
   u32x4 v[Cfg<T>::kBf16 ? NVU * 4 : NK];
 };
 
-// Load one 64-key tile into registers. key_src(kappa) returns the row pointer of key kappa for
-// the K (or V) cache, or nullptr for a zero row.
+// Keys (0..63 within a tile) this thread loads: K chunk i covers key kkey(i), bytes part*16..+16 of
+// its row; bf16 V covers keys 4*kg..4*kg+3 at elements 8*dg..8*dg+7 (kg fastest across lanes).
+template <typename T, int D>
+struct TileMap {
+  static constexpr int CH = TileRegs<T, D>::CH;
+  __device__ static int kkey(int i) { return (static_cast<int>(threadIdx.x) + kThreads * i) / CH; }
+  __device__ static int kpart() { return static_cast<int>(threadIdx.x) % CH; }
+  __device__ static int vkey(int e) { return Cfg<T>::kBf16 ? 4 * (static_cast<int>(threadIdx.x) % 16) + e : 0; }
+  __device__ static int vdg() { return static_cast<int>(threadIdx.x) / 16; }
+  __device__ static bool von() { return static_cast<int>(threadIdx.x) < 16 * (D / 8); }
+};
+
+// Load one 64-key tile into registers. row(kappa) returns the row of key kappa (0..63 within the tile)
+// of the K (or V) cache; it must always be a valid address (callers clamp out-of-range keys to the
+// last valid key -- those keys are masked, so their contents never reach the result).
 template <typename T, int D, typename KF, typename VF>
-__device__ __forceinline__ void load_tile(TileRegs<T, D> &r, KF key_src, VF val_src) {
-  constexpr int CH = TileRegs<T, D>::CH;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void load_tile(TileRegs<T, D> &r, KF key_row, VF val_row) {
+  using M = TileMap<T, D>;
+  constexpr int E = 16 / sizeof(T);
 #pragma unroll
-  for (int i = 0; i < TileRegs<T, D>::NK; ++i) {
-    const int c = tid + kThreads * i;
-    const int key = c / CH, part = c % CH;
-    const T *src = key_src(key);
-    r.k[i] = src ? *reinterpret_cast<const u32x4 *>(src + part * (16 / sizeof(T))) : u32x4{0, 0, 0, 0};
-  }
+  for (int i = 0; i < TileRegs<T, D>::NK; ++i)
+    r.k[i] = *reinterpret_cast<const u32x4 *>(key_row(M::kkey(i)) + M::kpart() * E);
   if constexpr (Cfg<T>::kBf16) {
+    static_assert(TileRegs<T, D>::NVU == 1, "one V unit per thread");
+    if (M::von()) {
 #pragma unroll
-    for (int i = 0; i < TileRegs<T, D>::NVU; ++i) {
-      const int u = tid + kThreads * i;
-      const int kg = u / (D / 8), dg = u % (D / 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const T *src = u < 16 * (D / 8) ? val_src(4 * kg + e) : nullptr;
-        r.v[4 * i + e] = src ? *reinterpret_cast<const u32x4 *>(src + dg * 8) : u32x4{0, 0, 0, 0};
-      }
+      for (int e = 0; e < 4; ++e)
+        r.v[e] = *reinterpret_cast<const u32x4 *>(val_row(M::vkey(e)) + M::vdg() * 8);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < TileRegs<T, D>::NK; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / CH, part = c % CH;
-      const T *src = val_src(key);
-      r.v[i] = src ? *reinterpret_cast<const u32x4 *>(src + part * (16 / sizeof(T))) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < TileRegs<T, D>::NK; ++i)
+      r.v[i] = *reinterpret_cast<const u32x4 *>(val_row(M::kkey(i)) + M::kpart() * E);
   }
 }
 
@@ -180,19 +174,16 @@ __device__ __forceinline__ void store_tile(const TileRegs<T, D> &r, T *ks, T *vs
     for (int i = 0; i < TileRegs<T, D>::NVU; ++i) {
       const int u = tid + kThreads * i;
       if (u >= 16 * (D / 8)) break;
-      const int kg = u / (D / 8), dg = u % (D / 8);
+      const int kg = u % 16, dg = u / 16;
       const int col = vt_col(4 * kg);
-      const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r.v[4 * i + 0]);
-      const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r.v[4 * i + 1]);
-      const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&r.v[4 * i + 2]);
-      const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&r.v[4 * i + 3]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        // element e of keys 4kg..4kg+3 -> four consecutive bf16 in row d = 8dg + e
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t a0 = (w0[e >> 1] >> sh) & 0xffffu, a1 = (w1[e >> 1] >> sh) & 0xffffu;
-        const uint32_t a2 = (w2[e >> 1] >> sh) & 0xffffu, a3 = (w3[e >> 1] >> sh) & 0xffffu;
-        u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
+        // element e of keys 4kg..4kg+3 -> four consecutive bf16 in row d = 8dg + e: one byte permute
+        // per output word picks the matching 16-bit halves of two keys' words
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x2 pk = {__builtin_amdgcn_perm(r.v[4 * i + 1][w], r.v[4 * i + 0][w], sel),
+                    __builtin_amdgcn_perm(r.v[4 * i + 3][w], r.v[4 * i + 2][w], sel)};
         *reinterpret_cast<u32x2 *>(vs + (8 * dg + e) * L::VS + col) = pk;
       }
     }
@@ -224,14 +215,16 @@ __device__ __forceinline__ void tile_step(const T *ks, const T *vs, const QF &qf
   const int col = lane & 31, hh = lane >> 5;
   f32x16 s[2] = {};
   if constexpr (Cfg<T>::kBf16) {
+    bf16x8 kfr[2][D / 16];  // all K fragments of the tile read before the MFMA chain
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(ks + (mb * 32 + col) * L::KS + kk * 16 + hh * 8);
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[mb], 0, 0, 0);
-      }
-    }
+      for (int mb = 0; mb < 2; ++mb)
+        kfr[mb][kk] = *reinterpret_cast<const bf16x8 *>(ks + (mb * 32 + col) * L::KS + kk * 16 + hh * 8);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[mb][kk], qf[kk], s[mb], 0, 0, 0);
   } else {
     const float *kf = reinterpret_cast<const float *>(ks);
 #pragma unroll
@@ -260,7 +253,16 @@ __device__ __forceinline__ void tile_step(const T *ks, const T *vs, const QF &qf
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(st.m, mx * c);
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  // The running max only moves for some lanes on some tiles; when it moves for no lane of the
+  // wavefront the rescale factor is exactly 1 and the O rescale is skipped.
+  if (__ballot(m_new > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    st.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
+  }
   float psum = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -270,23 +272,22 @@ __device__ __forceinline__ void tile_step(const T *ks, const T *vs, const QF &qf
       s[mb][r] = p;
       psum += p;
     }
-  st.l = st.l * alpha + psum;
+  st.l += psum;
   st.m = m_new;
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[b][r] *= alpha;
   if constexpr (Cfg<T>::kBf16) {
+    bf16x8 vfr[4][D / 32];  // all V^T fragments of the tile
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+        vfr[t][b] = *reinterpret_cast<const bf16x8 *>(vs + (b * 32 + col) * L::VS + t * 16 + hh * 8);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[t >> 1][8 * (t & 1) + i]);
 #pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vs + (b * 32 + col) * L::VS + t * 16 + hh * 8);
-        st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.o[b], 0, 0, 0);
-      }
+      for (int b = 0; b < D / 32; ++b) st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t][b], pb, st.o[b], 0, 0, 0);
     }
   } else {
     const float *vf = reinterpret_cast<const float *>(vs);
@@ -311,8 +312,10 @@ __device__ __forceinline__ int find_entry(const AttnArgs &a, int gamma) {
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
   using L = Lds<T, D>;
-  __shared__ __attribute__((aligned(16))) T ks[L::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) T vs[L::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) T ks2[2][L::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) T vs2[2][L::V_ELEMS];
+  T *ks = ks2[0];
+  T *vs = vs2[0];
   __shared__ int sh_row[kKeys];
   __shared__ int sh_blk[kKeys];
   __shared__ int sh_pos[kKeys];
@@ -374,29 +377,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
   const T *kc = static_cast<const T *>(a.k_cache);
   const T *vc = static_cast<const T *>(a.v_cache);
 
-  // ---- prefix phase ----
+  // ---- prefix phase: double-buffered 64-key tiles, one barrier per tile ----
   if (k1 > k0) {
+    const size_t rs = static_cast<size_t>(a.Hkv) * D;  // elements between consecutive tokens
+    const T *kb = kc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + g) * D;
+    const T *vb = vc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + g) * D;
+    // row of prefix token jj (clamped to the last token of this split's range)
+    auto row_at = [&](const T *flat, const T *cache, int jj) -> const T * {
+      jj = min(jj, k1 - 1);
+      if (!PAGED) return flat + jj * rs;
+      int page = a.page_table[static_cast<size_t>(R.req) * a.max_pages + jj / a.page_size];
+      page = min(max(page, 0), a.num_pages - 1);
+      return cache + ((static_cast<size_t>(page) * a.page_size + (jj % a.page_size)) * a.Hkv + g) * D;
+    };
     TileRegs<T, D> regs;
-    auto ksrc = [&](int kt) {
-      return [&, kt](int kappa) -> const T * {
-        const int jj = kt + kappa;
-        return jj < k1 ? kv_row(a, kc, R, jj, g, D, PAGED) : nullptr;
-      };
-    };
-    auto vsrc = [&](int kt) {
-      return [&, kt](int kappa) -> const T * {
-        const int jj = kt + kappa;
-        return jj < k1 ? kv_row(a, vc, R, jj, g, D, PAGED) : nullptr;
-      };
-    };
-    load_tile<T, D>(regs, ksrc(k0), vsrc(k0));
+    load_tile<T, D>(regs, [&](int kappa) { return row_at(kb, kc, k0 + kappa); },
+                    [&](int kappa) { return row_at(vb, vc, k0 + kappa); });
+    store_tile<T, D>(regs, ks2[0], vs2[0]);
+    __syncthreads();
+    int stage = 0;
     for (int kt = k0; kt < k1; kt += kKeys) {
-      __syncthreads();
-      store_tile<T, D>(regs, ks, vs);
-      __syncthreads();
-      if (kt + kKeys < k1) load_tile<T, D>(regs, ksrc(kt + kKeys), vsrc(kt + kKeys));
+      const int nk = kt + kKeys;
+      if (nk < k1)
+        load_tile<T, D>(regs, [&](int kappa) { return row_at(kb, kc, nk + kappa); },
+                        [&](int kappa) { return row_at(vb, vc, nk + kappa); });
       const int lim = k1 - kt;
-      tile_step<T, D>(ks, vs, qf, st, c, lim < kKeys, [&](int key) { return key < lim; });
+      tile_step<T, D>(ks2[stage], vs2[stage], qf, st, c, lim < kKeys, [&](int key) { return key < lim; });
+      if (nk < k1) store_tile<T, D>(regs, ks2[stage ^ 1], vs2[stage ^ 1]);
+      __syncthreads();
+      stage ^= 1;
     }
   }
 
@@ -427,8 +436,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
       TileRegs<T, D> regs;
       auto src = [&](const T *base) {
         return [&, base](int kappa) -> const T * {
-          const int rr = sh_row[kappa];
-          return rr < 0 ? nullptr : base + (static_cast<size_t>(R.q_begin + rr) * a.Hkv + g) * D;
+          const int rr = max(sh_row[kappa], 0);  // unused slots read row 0 of the request; masked
+          return base + (static_cast<size_t>(R.q_begin + rr) * a.Hkv + g) * D;
         };
       };
       load_tile<T, D>(regs, src(kn), src(vn));
@@ -486,44 +495,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
   }
 }
 
-// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. One wavefront per row.
+// Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. Each thread owns four
+// consecutive elements of one row (16-byte loads); D/4 threads per row.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  constexpr int TPR = D / 4;  // threads per row
+  const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
+  const int d0 = (threadIdx.x % TPR) * 4;
   if (row >= a.comb_rows) return;
-  int e = -1;
+  int e = 0;
   for (int i = 0; i < a.n_entries; ++i) {
     const ReqInfo &R = a.req[i];
     if (R.n_splits > 1 && row >= R.comb_begin && row < R.comb_begin + R.n_q * a.Hq) e = i;
   }
-  if (e < 0) return;
-  const ReqInfo R = a.req[e];
+  const ReqInfo &R = a.req[e];
   const int local = row - R.comb_begin;
   const int q_local = local / a.Hq, h = local - q_local * a.Hq;
+  const size_t stride = static_cast<size_t>(R.n_q) * a.Hq;  // slots between consecutive splits
+  const size_t slot0 = static_cast<size_t>(R.part_begin) + static_cast<size_t>(q_local) * a.Hq + h;
   float M = -INFINITY;
-  for (int s = 0; s < R.n_splits; ++s) {
-    const size_t slot = static_cast<size_t>(R.part_begin) + (static_cast<size_t>(s) * R.n_q + q_local) * a.Hq + h;
-    M = fmaxf(M, a.part_ml[slot * 2]);
-  }
-  constexpr int E = D / 64;
-  float acc[E] = {};
+  for (int s = 0; s < R.n_splits; ++s) M = fmaxf(M, a.part_ml[(slot0 + s * stride) * 2]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
+#pragma unroll 4
   for (int s = 0; s < R.n_splits; ++s) {
-    const size_t slot = static_cast<size_t>(R.part_begin) + (static_cast<size_t>(s) * R.n_q + q_local) * a.Hq + h;
+    const size_t slot = slot0 + s * stride;
     const float wgt = __builtin_amdgcn_exp2f(a.part_ml[slot * 2] - M);
     lsum += wgt * a.part_ml[slot * 2 + 1];
+    const f32x4 o = *reinterpret_cast<const f32x4 *>(a.part_o + slot * D + d0);
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[i] += wgt * a.part_o[slot * D + lane * E + i];
+    for (int k = 0; k < 4; ++k) acc[k] += wgt * o[k];
   }
   const float inv = 1.f / lsum;
   const size_t orow = static_cast<size_t>(R.q_begin + q_local) * a.Hq + h;
+  if constexpr (Cfg<T>::kBf16) {
+    bf16x4 v4;
 #pragma unroll
-  for (int i = 0; i < E; ++i) {
-    if constexpr (Cfg<T>::kBf16)
-      static_cast<__bf16 *>(a.out)[orow * D + lane * E + i] = static_cast<__bf16>(acc[i] * inv);
-    else
-      static_cast<float *>(a.out)[orow * D + lane * E + i] = acc[i] * inv;
+    for (int k = 0; k < 4; ++k) v4[k] = static_cast<__bf16>(acc[k] * inv);
+    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(a.out) + orow * D + d0) = v4;
+  } else {
+    f32x4 v4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v4[k] = acc[k] * inv;
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow * D + d0) = v4;
   }
 }
 
@@ -575,7 +589,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
       len[i] = 0;
       continue;
     }
-    long long s = std::min<long long>(factor, std::max(1, pre[i] / kMinSplit));
+    long long s = std::min<long long>(std::min<long long>(factor, kMaxSplits), std::max(1, pre[i] / kMinSplit));
     int l = static_cast<int>((pre[i] + s - 1) / s);
     l = (l + kKeys - 1) / kKeys * kKeys;
     len[i] = l;
@@ -620,7 +634,8 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   a.t_max = t_max;
   a.comb_rows = comb;
   P->grid = kXcds * ((groups + kXcds - 1) / kXcds) * t_max;
-  P->comb_grid = (comb + kThreads / 64 - 1) / (kThreads / 64);
+  const int rows_per_block = kThreads / (D / 4);
+  P->comb_grid = (comb + rows_per_block - 1) / rows_per_block;
   P->part_slots = part;
   P->ws_bytes = part ? align_up(part * D * sizeof(float), 256) + align_up(part * 2 * sizeof(float), 256) : 0;
   return D3D_OK;

@@ -11,25 +11,34 @@
 namespace d3d {
 namespace {
 
-__global__ __launch_bounds__(64) void match_kernel(const d3d_block_desc *descs, int total_blocks,
-                                                   const int32_t *off, int n_req,
-                                                   const int32_t *n_acc, const int32_t *next,
-                                                   int32_t *hit) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// One wavefront per request: lanes test 64 consecutive blocks at a time; the lowest matching lane
+// of the first window that has one is the first hit in pack order.
+__global__ __launch_bounds__(256) void match_kernel(const d3d_block_desc *descs, int total_blocks,
+                                                    const int32_t *off, int n_req,
+                                                    const int32_t *n_acc, const int32_t *next,
+                                                    int32_t *hit) {
+  const int i = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (i >= n_req) return;
   const int b0 = min(max(off[i], 0), total_blocks);
   const int b1 = min(max(off[i + 1], b0), total_blocks);
   const int want_r = n_acc[i] + 1;
   const int tok = next[i];
   int found = -1;
-  for (int b = b0 + 1; b < b1; ++b) {
-    const d3d_block_desc d = descs[b];
-    if (d.rej_pos == want_r && d.anchor == tok) {
-      found = b - b0;
+  for (int base = b0 + 1; base < b1; base += 64) {
+    const int b = base + lane;
+    bool m = false;
+    if (b < b1) {
+      const d3d_block_desc d = descs[b];
+      m = d.rej_pos == want_r && d.anchor == tok;
+    }
+    const unsigned long long bal = __ballot(m);
+    if (bal) {
+      found = base + (__ffsll(static_cast<long long>(bal)) - 1) - b0;
       break;
     }
   }
-  hit[i] = found;
+  if (lane == 0) hit[i] = found;
 }
 
 }  // namespace
@@ -41,8 +50,8 @@ extern "C" int branch_cache_match(const d3d_block_desc *descs, int total_blocks,
                                   int32_t *hit_branch, hipStream_t stream) {
   if (!descs || !req_block_off || !n_accepted || !next_token || !hit_branch) return D3D_EINVAL;
   if (n_req < 1 || total_blocks < 1) return D3D_EINVAL;
-  const int threads = 64;
-  d3d::match_kernel<<<(n_req + threads - 1) / threads, threads, 0, stream>>>(
+  const int per_block = 4;  // requests (wavefronts) per workgroup
+  d3d::match_kernel<<<(n_req + per_block - 1) / per_block, 64 * per_block, 0, stream>>>(
       descs, total_blocks, req_block_off, n_req, n_accepted, next_token, hit_branch);
   return d3d::launch_status();
 }

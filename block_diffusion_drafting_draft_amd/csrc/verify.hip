@@ -222,91 +222,113 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
 // ------------------------------------------------------------------------------------------------
 // 2. decide
 // ------------------------------------------------------------------------------------------------
+// Merge one row's chunk partials with one wavefront (lanes stride over chunks): exact max, first
+// argmax, and the fp64 sum of exp((z - max)/T) rescaled from each chunk's own max.
 struct RowStat {
   float max;
   double sum;
   int arg;
 };
 
-__device__ RowStat merge_row(const VerifyArgs &a, int row) {
+__device__ RowStat merge_row_wave(const VerifyArgs &a, int row) {
+  const int lane = threadIdx.x & 63;
   const StatPartial *p = a.stats + static_cast<size_t>(row) * a.chunks;
   float m = -INFINITY;
   int arg = INT_MAX;
-  for (int c = 0; c < a.chunks; ++c) {
-    if (p[c].max > m) {
-      m = p[c].max;
-      arg = p[c].arg;
-    }
-  }
   double s = 0.0;
-  if (!a.greedy)
-    for (int c = 0; c < a.chunks; ++c) s += p[c].sum * exp(static_cast<double>(p[c].max - m) * a.inv_t);
+  for (int c = lane; c < a.chunks; c += 64) {
+    const StatPartial q = p[c];
+    if (q.max > m) {  // chunks are visited in increasing order: keep the first maximum
+      if (!a.greedy && m != -INFINITY) s *= exp(static_cast<double>(m - q.max) * a.inv_t);
+      m = q.max;
+      arg = q.arg;
+    }
+    if (!a.greedy) s += q.sum * exp(static_cast<double>(q.max - m) * a.inv_t);
+  }
+  float wm = m;
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+  int warg = m == wm ? arg : INT_MAX;
+  for (int o = 32; o > 0; o >>= 1) warg = min(warg, __shfl_xor(warg, o));
+  double ws = 0.0;
+  if (!a.greedy) {
+    ws = m == -INFINITY ? 0.0 : s * exp(static_cast<double>(m - wm) * a.inv_t);
+    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+  }
   RowStat r;
-  r.max = m;
-  r.sum = s;
-  r.arg = arg;
+  r.max = wm;
+  r.sum = ws;
+  r.arg = warg;
   return r;
 }
 
+// One workgroup per request. Local rows 0..nd are the target rows, nd+1..2nd the draft rows.
+constexpr int kDecideThreads = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(64) void decide_kernel(const VerifyArgs a) {
-  __shared__ double sh_alpha[64];
-  __shared__ double sh_u[64];
-  __shared__ int sh_arg[64];
-  __shared__ float sh_maxp[64];
-  __shared__ float sh_maxq[64];
-  __shared__ double sh_surv[64];
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(const VerifyArgs a) {
+  __shared__ float sh_max[128];
+  __shared__ double sh_sum[128];
+  __shared__ int sh_arg[128];
   const int i = blockIdx.x;
-  const int j = threadIdx.x;
   const int nd = a.n_draft;
   const int V = a.vocab;
-  if (j <= nd) {
-    const RowStat rp = merge_row(a, i * (nd + 1) + j);
-    sh_arg[j] = rp.arg;
-    sh_maxp[j] = rp.max;
-    if (j < nd) {
-      const RowStat rq = a.greedy ? RowStat{0.f, 0.0, 0} : merge_row(a, a.n_tgt_rows + i * nd + j);
-      sh_maxq[j] = rq.max;
-      const int y = min(max(a.tokens[static_cast<size_t>(i) * nd + j], 0), V - 1);
-      double alpha;
-      if (a.greedy) {
-        alpha = (y == rp.arg) ? 1.0 : 0.0;
-      } else {
-        const T *zp = static_cast<const T *>(a.target) + (static_cast<size_t>(i) * (nd + 1) + j) * V;
-        const T *zq = static_cast<const T *>(a.draft) + (static_cast<size_t>(i) * nd + j) * V;
-        const double lp = (static_cast<double>(load_elem(zp + y)) - rp.max) * a.inv_t - log(rp.sum);
-        const double lq = (static_cast<double>(load_elem(zq + y)) - rq.max) * a.inv_t - log(rq.sum);
-        const double py = exp(lp), qy = exp(lq);
-        alpha = qy > 0.0 ? fmin(1.0, py / qy) : 1.0;
-      }
-      sh_alpha[j] = alpha;
-      sh_u[j] = philox_uniform(a.seed, static_cast<uint32_t>(j), static_cast<uint32_t>(i), a.round, 0u);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_rows = a.greedy ? nd + 1 : 2 * nd + 1;
+  for (int r = wave; r < n_rows; r += kDecideThreads / 64) {
+    const int row = r <= nd ? i * (nd + 1) + r : a.n_tgt_rows + i * nd + (r - nd - 1);
+    const RowStat st = merge_row_wave(a, row);
+    if (lane == 0) {
+      sh_max[r] = st.max;
+      sh_sum[r] = st.sum;
+      sh_arg[r] = st.arg;
     }
   }
   __syncthreads();
-  if (j == 0) {
-    int n_acc = nd;
-    uint32_t fl = 0;
-    double prod = 1.0, tau = 1.0;
-    for (int k = 0; k < nd; ++k) {
-      const double al = sh_alpha[k];
-      if (n_acc == nd) {
-        if (!a.greedy && fabs(sh_u[k] - al) < kNear) fl |= 1u;
-        if (!(sh_u[k] < al)) n_acc = k;
-      }
-      prod *= al;
-      sh_surv[k] = prod;
-      tau += prod;
+  if (wave != 0) return;
+  // lane j judges draft j
+  const int j = lane;
+  double alpha = 1.0, u = 1.0;
+  if (j < nd) {
+    const int y = min(max(a.tokens[static_cast<size_t>(i) * nd + j], 0), V - 1);
+    if (a.greedy) {
+      alpha = (y == sh_arg[j]) ? 1.0 : 0.0;
+    } else {
+      const T *zp = static_cast<const T *>(a.target) + (static_cast<size_t>(i) * (nd + 1) + j) * V;
+      const T *zq = static_cast<const T *>(a.draft) + (static_cast<size_t>(i) * nd + j) * V;
+      const double lp = (static_cast<double>(load_elem(zp + y)) - sh_max[j]) * a.inv_t - log(sh_sum[j]);
+      const double lq = (static_cast<double>(load_elem(zq + y)) - sh_max[nd + 1 + j]) * a.inv_t -
+                        log(sh_sum[nd + 1 + j]);
+      const double py = exp(lp), qy = exp(lq);
+      alpha = qy > 0.0 ? fmin(1.0, py / qy) : 1.0;
     }
+    u = philox_uniform(a.seed, static_cast<uint32_t>(j), static_cast<uint32_t>(i), a.round, 0u);
+  }
+  // first rejection: lowest lane with !(u < alpha)
+  const unsigned long long rej = __ballot(j < nd && !(u < alpha));
+  const int n_acc = rej ? __ffsll(static_cast<long long>(rej)) - 1 : nd;
+  const unsigned long long near = __ballot(!a.greedy && j < nd && j <= n_acc && fabs(u - alpha) < kNear);
+  // S(k) = prod_{j<k} alpha_j: inclusive prefix product over lanes
+  double surv = alpha;  // lanes >= nd hold 1
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(surv, o);
+    if (lane >= o) surv *= t;
+  }
+  double tsum = j < nd ? surv : 0.0;
+  for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o);
+  if (j < nd) {
+    if (a.alpha) a.alpha[static_cast<size_t>(i) * nd + j] = static_cast<float>(alpha);
+    if (a.survival) a.survival[static_cast<size_t>(i) * nd + j] = static_cast<float>(surv);
+  }
+  if (lane == 0) {
     a.n_acc[i] = n_acc;
-    if (a.tau) a.tau[i] = static_cast<float>(tau);
-    if (a.flags) a.flags[i] = fl;
+    if (a.tau) a.tau[i] = static_cast<float>(1.0 + tsum);
+    if (a.flags) a.flags[i] = near ? 1u : 0u;
     SampleState st;
     st.pad = 0;
     st.tgt_row = i * (nd + 1) + n_acc;
     st.drf_row = i * nd + min(n_acc, nd - 1);  // never read in bonus mode
-    st.max_p = sh_maxp[n_acc];
-    st.max_q = n_acc < nd ? sh_maxq[n_acc] : 0.f;
+    st.max_p = sh_max[n_acc];
+    st.max_q = (!a.greedy && n_acc < nd) ? sh_max[nd + 1 + n_acc] : 0.f;
     st.u = philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
     if (a.greedy) {
       st.mode = kDone;
@@ -316,11 +338,35 @@ __global__ __launch_bounds__(64) void decide_kernel(const VerifyArgs a) {
     }
     a.state[i] = st;
   }
-  __syncthreads();
-  if (j < nd) {
-    if (a.alpha) a.alpha[static_cast<size_t>(i) * nd + j] = static_cast<float>(sh_alpha[j]);
-    if (a.survival) a.survival[static_cast<size_t>(i) * nd + j] = static_cast<float>(sh_surv[j]);
-  }
+}
+
+// exp(x) in fp64 for x <= 0, the only arguments the sample passes produce (logits minus their row
+// max, or log-probabilities). Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software Manual
+// for the Elementary Functions", 1980): x = k ln2 + r with |r| <= ln2/2, ln2 split into a 21-bit
+// head (k * head is exact) and a tail; then the Taylor series of e^r to degree 12 (truncation below
+// 2e-16 relative) and a scaling by 2^k. About 18 fp64 operations.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  constexpr double kInvLn2 = 1.4426950408889634;
+  constexpr double kLn2Hi = 0.6931467056274414;      // ln 2 with its low 32 mantissa bits cleared
+  constexpr double kLn2Lo = 4.7493250390316726e-07;  // ln 2 - kLn2Hi
+  if (!(x > -745.5)) return 0.0;
+  const double k = rint(x * kInvLn2);
+  double r = fma(-k, kLn2Hi, x);
+  r = fma(-k, kLn2Lo, r);
+  double p = 2.08767569878681e-09;  // 1/12!
+  p = fma(p, r, 2.505210838544172e-08);
+  p = fma(p, r, 2.755731922398589e-07);
+  p = fma(p, r, 2.7557319223985893e-06);
+  p = fma(p, r, 2.48015873015873e-05);
+  p = fma(p, r, 0.0001984126984126984);
+  p = fma(p, r, 0.001388888888888889);
+  p = fma(p, r, 0.008333333333333333);
+  p = fma(p, r, 0.041666666666666664);
+  p = fma(p, r, 0.16666666666666666);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, static_cast<int>(k));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -342,10 +388,10 @@ struct DrawRows {
   // draw or the zero-mass fallback (mode != kResidual).
   __device__ __forceinline__ double mass(int v) const {
     const double ap = centered(p, v, mp, inv_t) - log_sp;
-    if (mode != kResidual) return exp(ap);
+    if (mode != kResidual) return exp_nonpos(ap);
     const double aq = centered(q, v, mq, inv_t) - log_sq;
-    if (!(ap > aq)) return 0.0;
-    return fmax(0.0, exp(ap) - exp(aq));
+    if (!(ap > aq)) return 0.0;  // P(v) <= Q(v): no residual mass, no exp needed
+    return fmax(0.0, exp_nonpos(ap) - exp_nonpos(aq));
   }
 };
 
@@ -362,8 +408,8 @@ __global__ __launch_bounds__(kThreads) void sample_lse_kernel(const VerifyArgs a
   const int end = min(begin + a.s_chunk_len, V);
   double sp = 0.0, sq = 0.0;
   for (int v = begin + threadIdx.x; v < end; v += kThreads) {
-    sp += exp(centered(p, v, st.max_p, a.inv_t));
-    if (st.mode == kResidual) sq += exp(centered(q, v, st.max_q, a.inv_t));
+    sp += exp_nonpos(centered(p, v, st.max_p, a.inv_t));
+    if (st.mode == kResidual) sq += exp_nonpos(centered(q, v, st.max_q, a.inv_t));
   }
   sp = block_sum(sp, sh_d);
   sq = block_sum(sq, sh_d);
@@ -411,10 +457,31 @@ __global__ __launch_bounds__(kThreads) void sample_mass_kernel(const VerifyArgs 
   if (threadIdx.x == 0) a.mass_part[static_cast<size_t>(i) * a.s_chunks + blockIdx.x] = r;
 }
 
-// Inside [begin, end): the smallest v with offset + C(v) > target, where each thread owns one
-// contiguous run of tokens. Exactly one thread owns the crossing (its exclusive prefix and its
-// prefix plus its own mass bracket the target, both sums rounded identically); if rounding leaves
-// no crossing, the thread holding the last positive mass returns its last positive token.
+// Block-wide exclusive prefix sum of one double per thread (256 threads); also returns the total.
+__device__ double block_excl_scan(double v, double *sh, double *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  double off = 0.0, tot = 0.0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wave) off += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  double excl = __shfl_up(incl, 1);
+  if (lane == 0) excl = 0.0;
+  *total = tot;
+  return off + excl;
+}
+
+// Inside [begin, end): the smallest v with offset + C(v) > target. Each thread owns one contiguous
+// run of tokens; the owner is the first thread whose inclusive prefix exceeds the target, and it
+// walks its run. If rounding leaves no crossing, the last token with positive mass is returned.
 struct Found {
   int v;
   double c_v, c_prev;
@@ -422,53 +489,41 @@ struct Found {
 
 template <typename T>
 __device__ Found scan_find(const DrawRows<T> &d, int begin, int end, double offset, double target,
-                           double *sh_pref) {
+                           double *sh_scan, int *sh_int) {
   __shared__ Found sh_found;
-  __shared__ int sh_owner;
-  __shared__ int sh_last;
   const int n = end - begin;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = begin + min(n, static_cast<int>(threadIdx.x) * per);
   const int hi = begin + min(n, (static_cast<int>(threadIdx.x) + 1) * per);
   double local = 0.0;
   for (int v = lo; v < hi; ++v) local += d.mass(v);
-  sh_pref[threadIdx.x] = local;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double run = offset;
-    int owner = -1, last = -1;
-    for (int t = 0; t < kThreads; ++t) {
-      const double here = sh_pref[t];
-      const double next = run + here;
-      if (owner < 0 && run <= target && next > target) owner = t;
-      if (here > 0.0) last = t;
-      sh_pref[t] = run;  // exclusive prefix
-      run = next;
-    }
-    sh_owner = owner;
-    sh_last = last;
+  double total;
+  const double start = offset + block_excl_scan(local, sh_scan, &total);
+  const int me = static_cast<int>(threadIdx.x);
+  const int owner = block_min_int(start + local > target ? me : INT_MAX, sh_int);
+  const int last = -block_min_int(local > 0.0 ? -me : INT_MAX, sh_int);
+  if (me == 0) {
     sh_found.v = -1;
     sh_found.c_v = offset;
     sh_found.c_prev = offset;
   }
   __syncthreads();
-  const int me = static_cast<int>(threadIdx.x);
-  const bool owner = me == sh_owner;
-  if (owner || (sh_owner < 0 && me == sh_last)) {
-    double c = sh_pref[me];
-    Found last{-1, c, c};
+  const bool is_owner = me == owner;
+  if (is_owner || (owner == INT_MAX && me == last)) {
+    double c = start;
+    Found lastpos{-1, c, c};
     Found hit{-1, c, c};
     for (int v = lo; v < hi; ++v) {
       const double prev = c;
       const double m = d.mass(v);
       c += m;
-      if (m > 0.0) last = Found{v, c, prev};
-      if (owner && c > target) {
+      if (m > 0.0) lastpos = Found{v, c, prev};
+      if (is_owner && c > target) {
         hit = Found{v, c, prev};
         break;
       }
     }
-    sh_found = hit.v >= 0 ? hit : last;
+    sh_found = hit.v >= 0 ? hit : lastpos;
   }
   __syncthreads();
   const Found f = sh_found;
@@ -479,56 +534,59 @@ __device__ Found scan_find(const DrawRows<T> &d, int begin, int end, double offs
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs a) {
   __shared__ double sh_d[kWaves];
-  __shared__ double sh_pref[kThreads];
+  __shared__ int sh_i[kWaves];
   __shared__ double sh_cum[kMaxSampleChunks];
-  __shared__ int sh_chunk;
   const int i = blockIdx.x;
   const SampleState st = a.state[i];
   if (st.mode == kDone) return;
   DrawRows<T> d = draw_rows<T>(a, st, i, sh_d);
   const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
-  for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) sh_cum[c] = mass[c];
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double run = 0.0;
-    for (int c = 0; c < a.s_chunks; ++c) {
-      run += sh_cum[c];
-      sh_cum[c] = run;  // inclusive
-    }
+  // inclusive prefix of the chunk masses: each thread owns 4 consecutive chunks
+  constexpr int CPT = kMaxSampleChunks / kThreads;
+  const int c0 = threadIdx.x * CPT;
+  double mine[CPT];
+  double run = 0.0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    mine[k] = c0 + k < a.s_chunks ? mass[c0 + k] : 0.0;
+    run += mine[k];
+  }
+  double z;
+  double base = block_excl_scan(run, sh_d, &z);
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    base += mine[k];
+    if (c0 + k < a.s_chunks) sh_cum[c0 + k] = base;
   }
   __syncthreads();
-  double z = sh_cum[a.s_chunks - 1];
   uint32_t fl = 0;
   Found f;
   if (!(z > 0.0)) {
     // zero residual mass (not reachable in exact arithmetic): draw from P instead
     fl |= 4u;
     d.mode = kBonus;
-    const double zp = [&] {
-      double s = 0.0;
-      for (int v = threadIdx.x; v < a.vocab; v += kThreads) s += d.mass(v);
-      return block_sum(s, sh_d);
-    }();
-    z = zp;
-    f = scan_find(d, 0, a.vocab, 0.0, st.u * z, sh_pref);
+    double s = 0.0;
+    for (int v = threadIdx.x; v < a.vocab; v += kThreads) s += d.mass(v);
+    z = block_sum(s, sh_d);
+    f = scan_find(d, 0, a.vocab, 0.0, st.u * z, sh_d, sh_i);
   } else {
     const double target = st.u * z;
-    if (threadIdx.x == 0) {
-      int c_star = -1, last_pos = -1;
-      double prev = 0.0;
-      for (int c = 0; c < a.s_chunks; ++c) {
-        if (sh_cum[c] > prev) last_pos = c;
-        if (c_star < 0 && sh_cum[c] > target) c_star = c;
-        prev = sh_cum[c];
+    int cand = INT_MAX, lastpos = -1;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = c0 + k;
+      if (c < a.s_chunks) {
+        if (cand == INT_MAX && sh_cum[c] > target) cand = c;
+        if (mine[k] > 0.0) lastpos = c;
       }
-      sh_chunk = c_star >= 0 ? c_star : last_pos;
     }
-    __syncthreads();
-    const int c = sh_chunk;
+    const int c_star = block_min_int(cand, sh_i);
+    const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
+    const int c = c_star != INT_MAX ? c_star : c_last;
     const double offset = c > 0 ? sh_cum[c - 1] : 0.0;
     const int begin = c * a.s_chunk_len;
     const int end = min(begin + a.s_chunk_len, a.vocab);
-    f = scan_find(d, begin, end, offset, target, sh_pref);
+    f = scan_find(d, begin, end, offset, target, sh_d, sh_i);
   }
   if (threadIdx.x == 0) {
     const double target = st.u * z;
@@ -594,7 +652,7 @@ int launch_verify(const VerifyArgs &a, bool vec, hipStream_t stream) {
     else
       stats_kernel<T, false, false><<<stat_grid, kThreads, 0, stream>>>(a);
   }
-  decide_kernel<T><<<a.n_req, 64, 0, stream>>>(a);
+  decide_kernel<T><<<a.n_req, kDecideThreads, 0, stream>>>(a);
   if (!a.greedy) {
     const dim3 s_grid(a.s_chunks, a.n_req);
     sample_lse_kernel<T><<<s_grid, kThreads, 0, stream>>>(a);

@@ -95,7 +95,8 @@ int d3d_build_branch_descs(int block_size, int coverage, int fanout, int prefix_
  *     page_table != NULL: [num_pages, page_size, n_heads_kv, head_dim]; token p of request i is row
  *                         p mod page_size of page page_table[i*max_pages + p/page_size]; needs
  *                         req_prefix_len[i] <= max_pages*page_size. Page ids outside
- *                         [0, num_pages) read as zero vectors.
+ *                         [0, num_pages) are clamped into range (the result is then unspecified,
+ *                         but no access leaves the cache).
  *  descs  [total_blocks] device descriptors (rej_pos and flags are used; rej_pos is clamped to
  *         [0, B]).
  *  req_block_off (host) [n_req+1], non-decreasing, req_block_off[0] == 0.

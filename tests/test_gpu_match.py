@@ -84,3 +84,55 @@ def test_one_device_round_async():
         assert int(res["n_accepted"][0]) == o.n_accepted and int(res["next_token"][0]) == o.next_token
         assert int(hit[0]) == o_match.match_request(blocks, o.n_accepted, o.next_token)
     _say(f"  n_acc={o.n_accepted} token={o.next_token} hit={int(hit[0])}")
+
+
+def test_graph_replays_match_eager():
+    """The device round captured in a HIP graph gives, on every replay, exactly the eager results
+    (the kernels are deterministic); eager work and synchronisations run between the replays."""
+    require_gpu()
+    _say("graph capture: replays vs eager")
+    B, C, F, L = 16, 4, 2, 300
+    w = synth.Workload("graph", "bf16", 32, 8, 128, B, C, F, (L,), 1, False, 4096, "zipf", 0.8, 1.0, 21, 0x77)
+    ain, vin = synth.attention_inputs(w), synth.verify_inputs(w)
+    prob = AttnProblem("bf16", B, [dict(L=L, kind="async", C=C, F=F, a0=int(vin["cur_anchor"][0]),
+                                        anchors=vin["alt_anchors"][0])], ain)
+    zt, zd = dev(vin["z_target"], "bf16"), dev(vin["z_draft"], "bf16")
+    tok = torch.from_numpy(vin["tokens"]).cuda()
+    off_dev = torch.tensor(prob.off, dtype=torch.int32).cuda()
+    out = torch.empty_like(prob.q)
+    need = _binding.draft_attn_packed_workspace(prob.off, prob.pre, B, 32, 8, 128)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    vws = torch.empty(_binding.spec_verify_workspace(1, B - 1, 4096), dtype=torch.uint8, device="cuda")
+    res = dict(n_accepted=torch.empty(1, dtype=torch.int32, device="cuda"),
+               next_token=torch.empty(1, dtype=torch.int32, device="cuda"),
+               alpha=torch.empty(1, B - 1, device="cuda"), survival=torch.empty(1, B - 1, device="cuda"),
+               tau=torch.empty(1, device="cuda"), flags=torch.empty(1, dtype=torch.int32, device="cuda"))
+    hit = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def device_round():
+        _binding.draft_attn_packed(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.descs,
+                                   prob.off, prob.pre, B, out=out, ws=ws)
+        _binding.spec_verify(zt, zd, tok, 1.0, 0x77, 3, ws=vws, out=res)
+        _binding.branch_cache_match(prob.descs, off_dev, res["n_accepted"], res["next_token"], hit=hit)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [out.clone(), hit.clone()] + [v.clone() for v in res.values()]
+
+    device_round()
+    eager = snapshot()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        device_round()
+    for rep in range(3):
+        out.zero_()
+        hit.fill_(-7)
+        for v in res.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for a, b in zip(eager, got):
+            assert torch.equal(a, b), rep
+        device_round()  # eager work between replays
+        torch.cuda.synchronize()
