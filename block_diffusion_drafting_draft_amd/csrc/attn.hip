@@ -12,23 +12,27 @@
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: Q stays in registers (the B operand)
 //    for the whole key walk, K and V come from LDS. The S^T accumulator leaves every lane holding one
 //    query column, so the softmax row max / sum are per-lane scalars (one cross-half exchange), and
-//    the accumulator registers are already the B operand of the PV product once the keys are
-//    permuted consistently: V is stored transposed in LDS with each 16-key group reordered so that
-//    the 8 keys a lane's accumulator holds are 8 contiguous bf16 (one 16-byte LDS read).
-//  * Prefix phase: 64-key tiles over the request's prefix, no mask except the ragged end; every
-//    packed query of the request shares this one walk (no per-branch prefix re-read).
-//  * In-pack tail: the keys of the request's current block and of the blocks the tile's queries
+//    the accumulator registers are already the B operand of the PV product.
+//  * bf16 tiles of 64 keys are copied global -> LDS by the LDS-DMA loads (global_load_lds, 16 bytes a
+//    lane, 1 KB a wavefront instruction): no register staging and no LDS store instructions. Rows are
+//    kept in natural [key][d] order with an XOR swizzle of the 16-byte chunks that keeps both read
+//    patterns below conflict-free. K fragments are plain 16-byte reads; V^T fragments come from the
+//    transposing LDS read ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one column
+//    -- exactly the key order the S^T accumulator holds, so no data is permuted anywhere.
+//  * Prefix phase: double-buffered tiles over the request's prefix (one barrier per tile), no mask
+//    except the ragged end; every packed query of the request shares this one walk.
+//  * In-pack tail: the rows of the request's current block and of the blocks the tile's queries
 //    belong to are gathered into 64-key tiles with a per-(row, key) visibility test from the block
 //    descriptors.
 //  * Split-KV: a request's prefix is cut into equal key ranges; each (request, split, kv head) is a
 //    "group" whose tiles share one key/value slice. Groups are dealt round-robin to the 8 XCDs so that
 //    all tiles of a group run on one XCD (its L2 serves the slice to all of them), longest first.
 //    Split partials (unnormalised O, running max, sum) are merged by a second kernel.
+//  * fp32 inputs take a register-staged variant of the same walk on v_mfma_f32_32x32x2f32.
 #include <float.h>
 #include <math.h>
 
 #include <algorithm>
-#include <type_traits>
 #include <vector>
 
 #include "d3d_internal.h"
@@ -76,7 +80,6 @@ struct AttnArgs {
 
 template <typename T>
 struct Cfg;
-
 template <>
 struct Cfg<__bf16> {
   static constexpr bool kBf16 = true;
@@ -86,115 +89,65 @@ struct Cfg<float> {
   static constexpr bool kBf16 = false;
 };
 
-// LDS row strides (elements). bf16: K [64][D+8], V^T [D][64+8]. f32: K [64][D+2], V [64][D+8].
-template <typename T, int D>
-struct Lds {
-  static constexpr bool kBf16 = Cfg<T>::kBf16;
-  static constexpr int KS = kBf16 ? D + 8 : D + 2;
-  static constexpr int VS = kBf16 ? kKeys + 8 : D + 8;
-  static constexpr int VROWS = kBf16 ? D : kKeys;
-  static constexpr int K_ELEMS = kKeys * KS;
-  static constexpr int V_ELEMS = VROWS * VS;
-};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(type, p) ((__attribute__((address_space(3))) type *)(p))
 
-// Column of key kappa (0..63) inside the transposed V tile: within each 16-key group, keys
-// {0-3, 8-11} -> columns 0-7 and {4-7, 12-15} -> columns 8-15, matching the keys one lane half of
-// the S^T accumulator holds.
-__device__ __forceinline__ int vt_col(int kappa) {
-  const int w = kappa & 15;
-  return (kappa & ~15) + 8 * ((w >> 2) & 1) + 4 * (w >> 3) + (w & 3);
+// ------------------------------------------------------------------------------------------------
+// work item, lane rows, softmax, output (shared by both element types)
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ int find_entry(const AttnArgs &a, int gamma) {
+  int e = 0;
+  while (e + 1 < a.n_entries && a.req[e + 1].group_begin <= gamma) ++e;
+  return e;
 }
 
-template <typename T, int D>
-struct TileRegs {
-  static constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
-  static constexpr int NK = kKeys * CH / kThreads;                  // K chunks per thread
-  // bf16 V is loaded as (4-key group, 8-element d group) units, 4-key group index fastest so that
-  // the transposed LDS stores of a wavefront half hit distinct banks; f32 V is loaded like K.
-  static constexpr int NVU = Cfg<T>::kBf16 ? (16 * (D / 8) + kThreads - 1) / kThreads : NK;
-  u32x4 k[NK];
-  u32x4 v[Cfg<T>::kBf16 ? NVU * 4 : NK];
+struct Item {
+  ReqInfo R;
+  int split, g, tile, k0, k1;
 };
 
-// Keys (0..63 within a tile) this thread loads: K chunk i covers key kkey(i), bytes part*16..+16 of
-// its row; bf16 V covers keys 4*kg..4*kg+3 at elements 8*dg..8*dg+7 (kg fastest across lanes).
-template <typename T, int D>
-struct TileMap {
-  static constexpr int CH = TileRegs<T, D>::CH;
-  __device__ static int kkey(int i) { return (static_cast<int>(threadIdx.x) + kThreads * i) / CH; }
-  __device__ static int kpart() { return static_cast<int>(threadIdx.x) % CH; }
-  __device__ static int vkey(int e) { return Cfg<T>::kBf16 ? 4 * (static_cast<int>(threadIdx.x) % 16) + e : 0; }
-  __device__ static int vdg() { return static_cast<int>(threadIdx.x) / 16; }
-  __device__ static bool von() { return static_cast<int>(threadIdx.x) < 16 * (D / 8); }
-};
-
-// Load one 64-key tile into registers. row(kappa) returns the row of key kappa (0..63 within the tile)
-// of the K (or V) cache; it must always be a valid address (callers clamp out-of-range keys to the
-// last valid key -- those keys are masked, so their contents never reach the result).
-template <typename T, int D, typename KF, typename VF>
-__device__ __forceinline__ void load_tile(TileRegs<T, D> &r, KF key_row, VF val_row) {
-  using M = TileMap<T, D>;
-  constexpr int E = 16 / sizeof(T);
-#pragma unroll
-  for (int i = 0; i < TileRegs<T, D>::NK; ++i)
-    r.k[i] = *reinterpret_cast<const u32x4 *>(key_row(M::kkey(i)) + M::kpart() * E);
-  if constexpr (Cfg<T>::kBf16) {
-    static_assert(TileRegs<T, D>::NVU == 1, "one V unit per thread");
-    if (M::von()) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r.v[e] = *reinterpret_cast<const u32x4 *>(val_row(M::vkey(e)) + M::vdg() * 8);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TileRegs<T, D>::NK; ++i)
-      r.v[i] = *reinterpret_cast<const u32x4 *>(val_row(M::kkey(i)) + M::kpart() * E);
-  }
+// XCD-aware mapping of the workgroup id: workgroup w runs on XCD w % 8; consecutive groups are
+// dealt round-robin to the XCDs and every tile of one group stays on the same XCD.
+__device__ __forceinline__ bool decode_item(const AttnArgs &a, Item &it) {
+  const int w = blockIdx.x;
+  const int x = w % kXcds, k = w / kXcds;
+  const int j = k / a.t_max;
+  it.tile = k - j * a.t_max;
+  const int gamma = j * kXcds + x;
+  if (gamma >= a.n_groups) return false;
+  it.R = a.req[find_entry(a, gamma)];
+  const int gl = gamma - it.R.group_begin;
+  it.split = gl / a.Hkv;
+  it.g = gl - it.split * a.Hkv;
+  if (it.tile >= (it.R.n_q + a.Qt - 1) / a.Qt) return false;
+  it.k0 = it.split * it.R.split_len;
+  it.k1 = min(it.R.prefix, it.k0 + it.R.split_len);
+  return true;
 }
 
-template <typename T, int D>
-__device__ __forceinline__ void store_tile(const TileRegs<T, D> &r, T *ks, T *vs) {
-  using L = Lds<T, D>;
-  constexpr int CH = TileRegs<T, D>::CH;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < TileRegs<T, D>::NK; ++i) {
-    const int c = tid + kThreads * i;
-    const int key = c / CH, part = c % CH;
-    if constexpr (Cfg<T>::kBf16) {
-      *reinterpret_cast<u32x4 *>(ks + key * L::KS + part * 8) = r.k[i];
-    } else {
-      float *dst = reinterpret_cast<float *>(ks) + key * L::KS + part * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(r.k[i][e]);
-    }
+struct LaneRow {
+  int q_local, h, blk, pos, r;
+  bool valid, causal;
+};
+
+__device__ __forceinline__ LaneRow lane_row(const AttnArgs &a, const Item &it) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = wave * 32 + (lane & 31);
+  const int head_local = row / a.Qt, qi = row - head_local * a.Qt;
+  LaneRow L;
+  L.q_local = it.tile * a.Qt + qi;
+  L.valid = L.q_local < it.R.n_q;
+  L.h = it.g * a.G + head_local;
+  L.blk = L.valid ? L.q_local / a.B : -1;
+  L.pos = L.valid ? L.q_local - L.blk * a.B : 0;
+  L.r = 0;
+  L.causal = false;
+  if (L.valid) {
+    const d3d_block_desc dsc = a.descs[it.R.block_begin + L.blk];
+    L.r = L.blk == 0 ? 0 : min(max(dsc.rej_pos, 0), a.B);
+    L.causal = (dsc.flags & D3D_BLOCK_CAUSAL) != 0;
   }
-  if constexpr (Cfg<T>::kBf16) {
-#pragma unroll
-    for (int i = 0; i < TileRegs<T, D>::NVU; ++i) {
-      const int u = tid + kThreads * i;
-      if (u >= 16 * (D / 8)) break;
-      const int kg = u % 16, dg = u / 16;
-      const int col = vt_col(4 * kg);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // element e of keys 4kg..4kg+3 -> four consecutive bf16 in row d = 8dg + e: one byte permute
-        // per output word picks the matching 16-bit halves of two keys' words
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 pk = {__builtin_amdgcn_perm(r.v[4 * i + 1][w], r.v[4 * i + 0][w], sel),
-                    __builtin_amdgcn_perm(r.v[4 * i + 3][w], r.v[4 * i + 2][w], sel)};
-        *reinterpret_cast<u32x2 *>(vs + (8 * dg + e) * L::VS + col) = pk;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TileRegs<T, D>::NK; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / CH, part = c % CH;
-      *reinterpret_cast<u32x4 *>(reinterpret_cast<float *>(vs) + key * L::VS + part * 4) = r.v[i];
-    }
-  }
+  return L;
 }
 
 // Per-wavefront online-softmax state for 32 query columns.
@@ -205,44 +158,19 @@ struct RowState {
   float l;  // this lane's half of the running sum
 };
 
-// One 64-key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
-// visible(key) -> bool decides masking for this lane's query column (key = 0..63 within tile).
-template <typename T, int D, typename QF, typename VIS>
-__device__ __forceinline__ void tile_step(const T *ks, const T *vs, const QF &qf, RowState<D> &st,
-                                          float c, bool need_mask, VIS visible) {
-  using L = Lds<T, D>;
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 31, hh = lane >> 5;
-  f32x16 s[2] = {};
-  if constexpr (Cfg<T>::kBf16) {
-    bf16x8 kfr[2][D / 16];  // all K fragments of the tile read before the MFMA chain
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        kfr[mb][kk] = *reinterpret_cast<const bf16x8 *>(ks + (mb * 32 + col) * L::KS + kk * 16 + hh * 8);
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[mb][kk], qf[kk], s[mb], 0, 0, 0);
-  } else {
-    const float *kf = reinterpret_cast<const float *>(ks);
-#pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const float a = kf[(mb * 32 + col) * L::KS + 2 * kk + hh];
-        s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, qf[kk], s[mb], 0, 0, 0);
-      }
-    }
-  }
+// Mask, online-softmax update of (m, l, O) and S -> P in place. The lane holds the keys
+// kappa = mb*32 + 8*(r/4) + 4*hh + r%4 of its query column.
+template <int D, typename VIS>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[2], RowState<D> &st, float c, bool need_mask,
+                                               VIS visible) {
+  const int hh = (threadIdx.x & 63) >> 5;
   if (need_mask) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = mb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (!visible(key)) s[mb][r] = -INFINITY;
+        s[mb][r] = visible(key) ? s[mb][r] : -INFINITY;
       }
   }
   float mx = -INFINITY;
@@ -274,188 +202,17 @@ __device__ __forceinline__ void tile_step(const T *ks, const T *vs, const QF &qf
     }
   st.l += psum;
   st.m = m_new;
-  if constexpr (Cfg<T>::kBf16) {
-    bf16x8 vfr[4][D / 32];  // all V^T fragments of the tile
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b)
-        vfr[t][b] = *reinterpret_cast<const bf16x8 *>(vs + (b * 32 + col) * L::VS + t * 16 + hh * 8);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[t >> 1][8 * (t & 1) + i]);
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b) st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t][b], pb, st.o[b], 0, 0, 0);
-    }
-  } else {
-    const float *vf = reinterpret_cast<const float *>(vs);
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = mb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-          st.o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[key * L::VS + b * 32 + col], s[mb][r], st.o[b], 0, 0, 0);
-      }
-  }
 }
 
-__device__ __forceinline__ int find_entry(const AttnArgs &a, int gamma) {
-  int e = 0;
-  while (e + 1 < a.n_entries && a.req[e + 1].group_begin <= gamma) ++e;
-  return e;
-}
-
-template <typename T, int D, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
-  using L = Lds<T, D>;
-  __shared__ __attribute__((aligned(16))) T ks2[2][L::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) T vs2[2][L::V_ELEMS];
-  T *ks = ks2[0];
-  T *vs = vs2[0];
-  __shared__ int sh_row[kKeys];
-  __shared__ int sh_blk[kKeys];
-  __shared__ int sh_pos[kKeys];
-
-  // ---- work item: XCD-aware mapping of the workgroup id onto (group, tile) ----
-  const int w = blockIdx.x;
-  const int x = w % kXcds, k = w / kXcds;
-  const int j = k / a.t_max, tile = k - j * a.t_max;
-  const int gamma = j * kXcds + x;
-  if (gamma >= a.n_groups) return;
-  const ReqInfo R = a.req[find_entry(a, gamma)];
-  const int gl = gamma - R.group_begin;
-  const int split = gl / a.Hkv, g = gl - split * a.Hkv;
-  const int n_tiles = (R.n_q + a.Qt - 1) / a.Qt;
-  if (tile >= n_tiles) return;
-  const int k0 = split * R.split_len;
-  const int k1 = min(R.prefix, k0 + R.split_len);
-
-  // ---- this lane's query row ----
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 31, hh = lane >> 5;
-  const int row = wave * 32 + col;
-  const int head_local = row / a.Qt, qi = row - head_local * a.Qt;
-  const int q_local = tile * a.Qt + qi;
-  const bool valid = q_local < R.n_q;
-  const int h = g * a.G + head_local;
-  const int b_lane = valid ? q_local / a.B : -1;
-  const int pos_lane = valid ? q_local - b_lane * a.B : 0;
-  int r_lane = 0;
-  bool causal_lane = false;
-  if (valid) {
-    const d3d_block_desc dsc = a.descs[R.block_begin + b_lane];
-    r_lane = b_lane == 0 ? 0 : min(max(dsc.rej_pos, 0), a.B);
-    causal_lane = (dsc.flags & D3D_BLOCK_CAUSAL) != 0;
-  }
-
-  // ---- Q fragment (B operand), resident for the whole walk ----
-  using QFrag = typename std::conditional<Cfg<T>::kBf16, bf16x8, float>::type;
-  constexpr int NQ = Cfg<T>::kBf16 ? D / 16 : D / 2;
-  QFrag qf[NQ];
-  {
-    const T *qrow = static_cast<const T *>(a.q) + (static_cast<size_t>(R.q_begin + q_local) * a.Hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < NQ; ++kk) {
-      if constexpr (Cfg<T>::kBf16) {
-        qf[kk] = valid ? *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8) : bf16x8{};
-      } else {
-        qf[kk] = valid ? qrow[2 * kk + hh] : 0.f;
-      }
-    }
-  }
-
-  RowState<D> st;
-#pragma unroll
-  for (int b = 0; b < D / 32; ++b) st.o[b] = f32x16{};
-  st.m = -INFINITY;
-  st.l = 0.f;
-  const float c = a.scale_log2;
-  const T *kc = static_cast<const T *>(a.k_cache);
-  const T *vc = static_cast<const T *>(a.v_cache);
-
-  // ---- prefix phase: double-buffered 64-key tiles, one barrier per tile ----
-  if (k1 > k0) {
-    const size_t rs = static_cast<size_t>(a.Hkv) * D;  // elements between consecutive tokens
-    const T *kb = kc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + g) * D;
-    const T *vb = vc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + g) * D;
-    // row of prefix token jj (clamped to the last token of this split's range)
-    auto row_at = [&](const T *flat, const T *cache, int jj) -> const T * {
-      jj = min(jj, k1 - 1);
-      if (!PAGED) return flat + jj * rs;
-      int page = a.page_table[static_cast<size_t>(R.req) * a.max_pages + jj / a.page_size];
-      page = min(max(page, 0), a.num_pages - 1);
-      return cache + ((static_cast<size_t>(page) * a.page_size + (jj % a.page_size)) * a.Hkv + g) * D;
-    };
-    TileRegs<T, D> regs;
-    load_tile<T, D>(regs, [&](int kappa) { return row_at(kb, kc, k0 + kappa); },
-                    [&](int kappa) { return row_at(vb, vc, k0 + kappa); });
-    store_tile<T, D>(regs, ks2[0], vs2[0]);
-    __syncthreads();
-    int stage = 0;
-    for (int kt = k0; kt < k1; kt += kKeys) {
-      const int nk = kt + kKeys;
-      if (nk < k1)
-        load_tile<T, D>(regs, [&](int kappa) { return row_at(kb, kc, nk + kappa); },
-                        [&](int kappa) { return row_at(vb, vc, nk + kappa); });
-      const int lim = k1 - kt;
-      tile_step<T, D>(ks2[stage], vs2[stage], qf, st, c, lim < kKeys, [&](int key) { return key < lim; });
-      if (nk < k1) store_tile<T, D>(regs, ks2[stage ^ 1], vs2[stage ^ 1]);
-      __syncthreads();
-      stage ^= 1;
-    }
-  }
-
-  // ---- in-pack tail (first split only) ----
-  if (split == 0) {
-    const int tq0 = tile * a.Qt;
-    const int tq1 = min(R.n_q, tq0 + a.Qt);
-    const int bf = tq0 / a.B, bl = (tq1 - 1) / a.B;
-    const int first = max(bf, 1);
-    const int n_list = a.B + max(0, bl - first + 1) * a.B;
-    const T *kn = static_cast<const T *>(a.k_new);
-    const T *vn = static_cast<const T *>(a.v_new);
-    for (int kt = 0; kt < n_list; kt += kKeys) {
-      __syncthreads();
-      if (threadIdx.x < kKeys) {
-        const int kappa = kt + threadIdx.x;
-        int rr = -1, blk = -1, pos = 0;
-        if (kappa < n_list) {
-          rr = kappa < a.B ? kappa : first * a.B + (kappa - a.B);
-          blk = rr / a.B;
-          pos = rr - blk * a.B;
-        }
-        sh_row[threadIdx.x] = rr;
-        sh_blk[threadIdx.x] = blk;
-        sh_pos[threadIdx.x] = pos;
-      }
-      __syncthreads();
-      TileRegs<T, D> regs;
-      auto src = [&](const T *base) {
-        return [&, base](int kappa) -> const T * {
-          const int rr = max(sh_row[kappa], 0);  // unused slots read row 0 of the request; masked
-          return base + (static_cast<size_t>(R.q_begin + rr) * a.Hkv + g) * D;
-        };
-      };
-      load_tile<T, D>(regs, src(kn), src(vn));
-      store_tile<T, D>(regs, ks, vs);
-      __syncthreads();
-      tile_step<T, D>(ks, vs, qf, st, c, true, [&](int key) {
-        const int blk = sh_blk[key];
-        if (blk < 0) return false;
-        if (blk == b_lane) return !causal_lane || sh_pos[key] <= pos_lane;
-        return blk == 0 && sh_pos[key] < r_lane;
-      });
-    }
-  }
-
-  // ---- write ----
+// Final write: the normalised output (single split) or the split partial (unnormalised O, m, l).
+template <typename T, int D>
+__device__ __forceinline__ void write_result(const AttnArgs &a, const Item &it, const LaneRow &L,
+                                             const RowState<D> &st) {
+  const int hh = (threadIdx.x & 63) >> 5;
   const float l_tot = st.l + __shfl_xor(st.l, 32);
-  if (!valid) return;
-  const size_t orow = static_cast<size_t>(R.q_begin + q_local) * a.Hq + h;
+  if (!L.valid) return;
+  const ReqInfo &R = it.R;
+  const size_t orow = static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h;
   if (R.n_splits == 1) {
     const float inv = 1.f / l_tot;
 #pragma unroll
@@ -477,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
       }
   } else {
     const size_t slot = static_cast<size_t>(R.part_begin) +
-                        (static_cast<size_t>(split) * R.n_q + q_local) * a.Hq + h;
+                        (static_cast<size_t>(it.split) * R.n_q + L.q_local) * a.Hq + L.h;
 #pragma unroll
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
@@ -493,6 +250,376 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnArgs a) {
       a.part_ml[slot * 2 + 1] = l_tot;
     }
   }
+}
+
+// In-pack tail of a tile: the list of packed rows (relative to the request) its queries may see --
+// the current block's B rows, then the rows of the tile's own blocks other than the current block.
+struct TailList {
+  int first, n;
+};
+
+__device__ __forceinline__ TailList tail_list(const AttnArgs &a, const Item &it) {
+  const int tq0 = it.tile * a.Qt;
+  const int tq1 = min(it.R.n_q, tq0 + a.Qt);
+  const int bf = tq0 / a.B, bl = (tq1 - 1) / a.B;
+  TailList t;
+  t.first = max(bf, 1);
+  t.n = a.B + max(0, bl - t.first + 1) * a.B;
+  return t;
+}
+
+// Fill the per-key tables of tail tile kt (threads 0..63): packed row, block and position of each
+// list slot (-1 block for slots past the list).
+__device__ __forceinline__ void tail_tables(const AttnArgs &a, const TailList &tl, int kt, int *sh_row,
+                                            int *sh_blk, int *sh_pos) {
+  if (threadIdx.x < kKeys) {
+    const int kappa = kt + threadIdx.x;
+    int rr = -1, blk = -1, pos = 0;
+    if (kappa < tl.n) {
+      rr = kappa < a.B ? kappa : tl.first * a.B + (kappa - a.B);
+      blk = rr / a.B;
+      pos = rr - blk * a.B;
+    }
+    sh_row[threadIdx.x] = rr;
+    sh_blk[threadIdx.x] = blk;
+    sh_pos[threadIdx.x] = pos;
+  }
+}
+
+// Visibility of tail key `key` for this lane's query row, evaluated without branches: the mask is
+// applied per accumulator register under divergent lanes, and a select chain keeps every lane on one
+// straight path (short-circuit branches here let the masked copy of S be lost on some lanes).
+__device__ __forceinline__ bool tail_visible(const LaneRow &L, const int *sh_blk, const int *sh_pos, int key) {
+  const int blk = sh_blk[key], pos = sh_pos[key];
+  const int own = static_cast<int>(blk == L.blk) & (static_cast<int>(!L.causal) | static_cast<int>(pos <= L.pos));
+  const int cur = static_cast<int>(blk == 0) & static_cast<int>(pos < L.r);
+  return (static_cast<int>(blk >= 0) & (own | cur)) != 0;
+}
+
+// ------------------------------------------------------------------------------------------------
+// bf16: LDS-DMA tiles, swizzled rows, transposing V reads
+// ------------------------------------------------------------------------------------------------
+// XOR swizzle of the 16-byte chunks of LDS row r. 256-byte rows (d = 128): chunk c of row r lives at
+// c ^ f(r) with f(r) = ((r & 3) << 2) | ((r >> 2) & 3) -- a bijection over any 16 aligned rows (the K
+// fragment reads: 16 rows, same chunk) that also puts the 4 aligned chunks of 4 consecutive rows in
+// distinct bank groups (the transposing V reads). 128-byte rows (d = 64) share a bank line in pairs:
+// f(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3) has the same two properties there.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int D>
+struct DmaTile {
+  static constexpr int RB = D * 2;                   // bytes per LDS row (one key, one head)
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int BYTES = kKeys * RB;           // one K or V tile
+  static constexpr int NI = BYTES / (kThreads * 16);  // DMA instructions per wavefront per tile
+  static constexpr int RPI = 64 / CH;                 // rows per DMA instruction
+};
+
+// Copy rows 0..63 of one tile into `lds` (wave-uniform base). row_ptr(r) returns the global row of
+// tile key r; lane `lane` of instruction q fills LDS chunk q*64 + lane, i.e. row q*RPI + lane/CH,
+// physical chunk lane % CH, whose logical chunk is (lane % CH) ^ swz(row).
+template <int D, typename RF>
+__device__ __forceinline__ void dma_tile(char *lds, RF row_ptr) {
+  using TT = DmaTile<D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < TT::NI; ++i) {
+    const int q = wave * TT::NI + i;
+    const int r = q * TT::RPI + lane / TT::CH;
+    const int c = (lane % TT::CH) ^ swz<D>(r);
+    const __bf16 *src = row_ptr(r) + c * 8;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src),
+                                     LDS_PTR(void, lds + q * 1024), 16, 0, 0);
+  }
+}
+
+// One 64-key tile from LDS: S^T = K Q^T, softmax, O^T += V^T P^T.
+template <int D, typename VIS>
+__device__ __forceinline__ void tile_step_dma(const char *kst, const char *vst, const bf16x8 (&qf)[D / 16],
+                                              RowState<D> &st, float c, bool need_mask, VIS visible) {
+  using TT = DmaTile<D>;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  f32x16 s[2] = {};
+  bf16x8 kfr[2][D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int row = mb * 32 + col;
+      kfr[mb][kk] = *reinterpret_cast<const bf16x8 *>(kst + row * TT::RB + (((2 * kk + hh) ^ swz<D>(row)) << 4));
+    }
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[mb][kk], qf[kk], s[mb], 0, 0, 0);
+  softmax_update<D>(s, st, c, need_mask, visible);
+  // V^T fragment (t, b): lane l gets column d = 32b + l%32 of keys 16t + 4hh + {0..3} (first read)
+  // and 16t + 8 + 4hh + {0..3} (second read); in its 16-lane group, lane j points at row
+  // 16t + 4hh + j/4 (+8), columns 32b + 16*((l>>4)&1) + 4*(j%4) .. +3.
+  const int j = lane & 15, dd = (lane >> 4) & 1;
+  bf16x8 vfr[4][D / 32];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+      const int doff = 32 * b + 16 * dd + 4 * (j & 3);
+      const int ch = doff >> 3, byte = (doff & 7) * 2;
+      const int r1 = 16 * t + 4 * hh + (j >> 2), r2 = r1 + 8;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(v4i16, vst + r1 * TT::RB + ((ch ^ swz<D>(r1)) << 4) + byte));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          LDS_PTR(v4i16, vst + r2 * TT::RB + ((ch ^ swz<D>(r2)) << 4) + byte));
+      const v4i16 both[2] = {lo, hi};
+      vfr[t][b] = *reinterpret_cast<const bf16x8 *>(both);
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[t >> 1][8 * (t & 1) + i]);
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t][b], pb, st.o[b], 0, 0, 0);
+  }
+}
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel_bf16(const AttnArgs a) {
+  using TT = DmaTile<D>;
+  // one LDS object per stage and operand, so that the DMA into one stage is provably independent of
+  // the reads of the other (no conservative wait between them)
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[TT::BYTES];
+  __shared__ int sh_row[kKeys];
+  __shared__ int sh_blk[kKeys];
+  __shared__ int sh_pos[kKeys];
+  Item it;
+  if (!decode_item(a, it)) return;
+  const ReqInfo &R = it.R;
+  const LaneRow L = lane_row(a, it);
+  const int hh = (threadIdx.x & 63) >> 5;
+  bf16x8 qf[D / 16];
+  {
+    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      qf[kk] = L.valid ? *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8) : bf16x8{};
+  }
+  RowState<D> st;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) st.o[b] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const float c = a.scale_log2;
+
+  // ---- prefix phase ----
+  if (it.k1 > it.k0) {
+    const size_t rs = static_cast<size_t>(a.Hkv) * D;
+    const __bf16 *kc = static_cast<const __bf16 *>(a.k_cache);
+    const __bf16 *vc = static_cast<const __bf16 *>(a.v_cache);
+    const __bf16 *kb = kc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D;
+    const __bf16 *vb = vc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D;
+    const int k1 = it.k1;
+    // global row of prefix token jj, clamped to the last token of this split's range (keys past the
+    // end are masked, so only their address matters)
+    auto row_at = [&](const __bf16 *flat, const __bf16 *cache, int jj) -> const __bf16 * {
+      jj = min(jj, k1 - 1);
+      if (!PAGED) return flat + jj * rs;
+      int page = a.page_table[static_cast<size_t>(R.req) * a.max_pages + jj / a.page_size];
+      page = min(max(page, 0), a.num_pages - 1);
+      return cache + ((static_cast<size_t>(page) * a.page_size + (jj % a.page_size)) * a.Hkv + it.g) * D;
+    };
+    auto issue = [&](char *kdst, char *vdst, int kt) {
+      dma_tile<D>(kdst, [&](int r) { return row_at(kb, kc, kt + r); });
+      dma_tile<D>(vdst, [&](int r) { return row_at(vb, vc, kt + r); });
+    };
+    // one tile: prefetch the next into the other stage, compute this one, then wait for the
+    // prefetch (own DMA) and for every wavefront (barrier)
+    auto body = [&](const char *kcur, const char *vcur, char *knext, char *vnext, int kt) {
+      if (kt + kKeys < k1) issue(knext, vnext, kt + kKeys);
+      const int lim = k1 - kt;
+      tile_step_dma<D>(kcur, vcur, qf, st, c, lim < kKeys, [&](int key) { return key < lim; });
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    issue(lds_k0, lds_v0, it.k0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = it.k0; kt < k1; kt += 2 * kKeys) {
+      body(lds_k0, lds_v0, lds_k1, lds_v1, kt);
+      if (kt + kKeys < k1) body(lds_k1, lds_v1, lds_k0, lds_v0, kt + kKeys);
+    }
+  }
+
+  // ---- in-pack tail (first split only) ----
+  if (it.split == 0) {
+    const TailList tl = tail_list(a, it);
+    const __bf16 *kn = static_cast<const __bf16 *>(a.k_new);
+    const __bf16 *vn = static_cast<const __bf16 *>(a.v_new);
+    for (int kt = 0; kt < tl.n; kt += kKeys) {
+      __syncthreads();
+      tail_tables(a, tl, kt, sh_row, sh_blk, sh_pos);
+      __syncthreads();
+      auto src = [&](const __bf16 *base) {
+        return [&, base](int r) -> const __bf16 * {
+          const int rr = max(sh_row[r], 0);  // unused slots read row 0 of the request; masked
+          return base + (static_cast<size_t>(R.q_begin + rr) * a.Hkv + it.g) * D;
+        };
+      };
+      dma_tile<D>(lds_k0, src(kn));
+      dma_tile<D>(lds_v0, src(vn));
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      tile_step_dma<D>(lds_k0, lds_v0, qf, st, c, true,
+                       [&](int key) { return tail_visible(L, sh_blk, sh_pos, key); });
+    }
+  }
+  write_result<__bf16, D>(a, it, L, st);
+}
+
+// ------------------------------------------------------------------------------------------------
+// fp32: register-staged tiles, padded LDS rows, v_mfma_f32_32x32x2f32
+// ------------------------------------------------------------------------------------------------
+template <int D>
+struct F32Tile {
+  static constexpr int KS = D + 2;  // padded K row (floats): 2-way-free bank pattern for the reads
+  static constexpr int VS = D + 8;  // padded V row (floats)
+  static constexpr int CH = D / 4;  // 16-byte chunks per row
+  static constexpr int NK = kKeys * CH / kThreads;
+};
+
+template <int D, typename RF>
+__device__ __forceinline__ void f32_load(u32x4 (&k)[F32Tile<D>::NK], u32x4 (&v)[F32Tile<D>::NK], RF key_row,
+                                         RF val_row) {
+  using TT = F32Tile<D>;
+#pragma unroll
+  for (int i = 0; i < TT::NK; ++i) {
+    const int cidx = threadIdx.x + kThreads * i;
+    const int key = cidx / TT::CH, part = cidx % TT::CH;
+    k[i] = *reinterpret_cast<const u32x4 *>(key_row(key) + part * 4);
+    v[i] = *reinterpret_cast<const u32x4 *>(val_row(key) + part * 4);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void f32_store(const u32x4 (&k)[F32Tile<D>::NK], const u32x4 (&v)[F32Tile<D>::NK],
+                                          float *ks, float *vs) {
+  using TT = F32Tile<D>;
+#pragma unroll
+  for (int i = 0; i < TT::NK; ++i) {
+    const int cidx = threadIdx.x + kThreads * i;
+    const int key = cidx / TT::CH, part = cidx % TT::CH;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ks[key * TT::KS + part * 4 + e] = __uint_as_float(k[i][e]);
+    *reinterpret_cast<u32x4 *>(vs + key * TT::VS + part * 4) = v[i];
+  }
+}
+
+template <int D, typename VIS>
+__device__ __forceinline__ void tile_step_f32(const float *ks, const float *vs, const float (&qf)[D / 2],
+                                              RowState<D> &st, float c, bool need_mask, VIS visible) {
+  using TT = F32Tile<D>;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  f32x16 s[2] = {};
+#pragma unroll
+  for (int kk = 0; kk < D / 2; ++kk)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+      s[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[(mb * 32 + col) * TT::KS + 2 * kk + hh], qf[kk], s[mb], 0, 0, 0);
+  softmax_update<D>(s, st, c, need_mask, visible);
+  // k-step (mb, r): lane half hh supplies key mb*32 + 8(r/4) + 4hh + r%4 -- the key its own
+  // accumulator register r holds
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = mb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+        st.o[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[key * TT::VS + b * 32 + col], s[mb][r], st.o[b], 0, 0, 0);
+    }
+}
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel_f32(const AttnArgs a) {
+  using TT = F32Tile<D>;
+  __shared__ __attribute__((aligned(16))) float ks[kKeys * TT::KS];
+  __shared__ __attribute__((aligned(16))) float vs[kKeys * TT::VS];
+  __shared__ int sh_row[kKeys];
+  __shared__ int sh_blk[kKeys];
+  __shared__ int sh_pos[kKeys];
+  Item it;
+  if (!decode_item(a, it)) return;
+  const ReqInfo &R = it.R;
+  const LaneRow L = lane_row(a, it);
+  const int hh = (threadIdx.x & 63) >> 5;
+  float qf[D / 2];
+  {
+    const float *qrow = static_cast<const float *>(a.q) + (static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) qf[kk] = L.valid ? qrow[2 * kk + hh] : 0.f;
+  }
+  RowState<D> st;
+#pragma unroll
+  for (int b = 0; b < D / 32; ++b) st.o[b] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const float c = a.scale_log2;
+  u32x4 kr[TT::NK], vr[TT::NK];
+  if (it.k1 > it.k0) {
+    const size_t rs = static_cast<size_t>(a.Hkv) * D;
+    const float *kc = static_cast<const float *>(a.k_cache);
+    const float *vc = static_cast<const float *>(a.v_cache);
+    const float *kb = kc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D;
+    const float *vb = vc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D;
+    const int k1 = it.k1;
+    for (int kt = it.k0; kt < k1; kt += kKeys) {
+      auto row_at = [&](const float *flat, const float *cache) {
+        return [&, flat, cache](int key) -> const float * {
+          const int jj = min(kt + key, k1 - 1);
+          if (!PAGED) return flat + jj * rs;
+          int page = a.page_table[static_cast<size_t>(R.req) * a.max_pages + jj / a.page_size];
+          page = min(max(page, 0), a.num_pages - 1);
+          return cache + ((static_cast<size_t>(page) * a.page_size + (jj % a.page_size)) * a.Hkv + it.g) * D;
+        };
+      };
+      f32_load<D>(kr, vr, row_at(kb, kc), row_at(vb, vc));
+      __syncthreads();
+      f32_store<D>(kr, vr, ks, vs);
+      __syncthreads();
+      const int lim = k1 - kt;
+      tile_step_f32<D>(ks, vs, qf, st, c, lim < kKeys, [&](int key) { return key < lim; });
+    }
+  }
+  if (it.split == 0) {
+    const TailList tl = tail_list(a, it);
+    const float *kn = static_cast<const float *>(a.k_new);
+    const float *vn = static_cast<const float *>(a.v_new);
+    for (int kt = 0; kt < tl.n; kt += kKeys) {
+      __syncthreads();
+      tail_tables(a, tl, kt, sh_row, sh_blk, sh_pos);
+      __syncthreads();
+      auto src = [&](const float *base) {
+        return [&, base](int r) -> const float * {
+          return base + (static_cast<size_t>(R.q_begin + max(sh_row[r], 0)) * a.Hkv + it.g) * D;
+        };
+      };
+      f32_load<D>(kr, vr, src(kn), src(vn));
+      f32_store<D>(kr, vr, ks, vs);
+      __syncthreads();
+      tile_step_f32<D>(ks, vs, qf, st, c, true, [&](int key) { return tail_visible(L, sh_blk, sh_pos, key); });
+    }
+  }
+  write_result<float, D>(a, it, L, st);
 }
 
 // Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. Each thread owns four
@@ -644,10 +771,17 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
 template <typename T, int D>
 void launch(const AttnPlan &P, bool paged, hipStream_t stream) {
   if (P.args.n_groups > 0) {
-    if (paged)
-      attn_kernel<T, D, true><<<P.grid, kThreads, 0, stream>>>(P.args);
-    else
-      attn_kernel<T, D, false><<<P.grid, kThreads, 0, stream>>>(P.args);
+    if constexpr (Cfg<T>::kBf16) {
+      if (paged)
+        attn_kernel_bf16<D, true><<<P.grid, kThreads, 0, stream>>>(P.args);
+      else
+        attn_kernel_bf16<D, false><<<P.grid, kThreads, 0, stream>>>(P.args);
+    } else {
+      if (paged)
+        attn_kernel_f32<D, true><<<P.grid, kThreads, 0, stream>>>(P.args);
+      else
+        attn_kernel_f32<D, false><<<P.grid, kThreads, 0, stream>>>(P.args);
+    }
   }
   if (P.args.comb_rows > 0) combine_kernel<T, D><<<P.comb_grid, kThreads, 0, stream>>>(P.args);
 }
