@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--workload", default="async-B16C12F2-L4096-V151936")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle's timed CPU work")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times (the reference "
+                        "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -200,6 +203,15 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
+        return 0
     w = synth.WORKLOADS[args.workload]
     r = Round(w)
     ring = [torch.empty_like(r.desc_host).pin_memory() for _ in range(3)]

@@ -75,6 +75,7 @@ struct AttnArgs {
   int B, Hq, Hkv, G, Qt;
   float scale_log2;
   int n_entries, n_groups, t_max, comb_rows;
+  int n_new;  // packed rows of k_new / v_new (all requests)
   ReqInfo req[D3D_ATTN_MAX_REQ];
 };
 
@@ -130,9 +131,9 @@ struct LaneRow {
   bool valid, causal;
 };
 
-__device__ __forceinline__ LaneRow lane_row(const AttnArgs &a, const Item &it) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = wave * 32 + (lane & 31);
+// Query row `row` (0..127) of the work item's 128 query-head rows: rows are head-major, Qt queries
+// of one head after another.
+__device__ __forceinline__ LaneRow lane_row(const AttnArgs &a, const Item &it, int row) {
   const int head_local = row / a.Qt, qi = row - head_local * a.Qt;
   LaneRow L;
   L.q_local = it.tile * a.Qt + qi;
@@ -207,9 +208,9 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[2], RowState<D> &st, 
 // Final write: the normalised output (single split) or the split partial (unnormalised O, m, l).
 template <typename T, int D>
 __device__ __forceinline__ void write_result(const AttnArgs &a, const Item &it, const LaneRow &L,
-                                             const RowState<D> &st) {
+                                             const f32x16 (&o)[D / 32], float m, float l) {
   const int hh = (threadIdx.x & 63) >> 5;
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  const float l_tot = l + __shfl_xor(l, 32);
   if (!L.valid) return;
   const ReqInfo &R = it.R;
   const size_t orow = static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h;
@@ -223,12 +224,12 @@ __device__ __forceinline__ void write_result(const AttnArgs &a, const Item &it, 
         if constexpr (Cfg<T>::kBf16) {
           bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(st.o[b][4 * r4 + e] * inv);
+          for (int e = 0; e < 4; ++e) v4[e] = static_cast<__bf16>(o[b][4 * r4 + e] * inv);
           *reinterpret_cast<bf16x4 *>(static_cast<T *>(a.out) + orow * D + d0) = v4;
         } else {
           f32x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = st.o[b][4 * r4 + e] * inv;
+          for (int e = 0; e < 4; ++e) v4[e] = o[b][4 * r4 + e] * inv;
           *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + orow * D + d0) = v4;
         }
       }
@@ -242,11 +243,11 @@ __device__ __forceinline__ void write_result(const AttnArgs &a, const Item &it, 
         const int d0 = b * 32 + 8 * r4 + 4 * hh;
         f32x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = st.o[b][4 * r4 + e];
+        for (int e = 0; e < 4; ++e) v4[e] = o[b][4 * r4 + e];
         *reinterpret_cast<f32x4 *>(a.part_o + slot * D + d0) = v4;
       }
     if (hh == 0) {
-      a.part_ml[slot * 2] = st.m;
+      a.part_ml[slot * 2] = m;
       a.part_ml[slot * 2 + 1] = l_tot;
     }
   }
@@ -297,13 +298,21 @@ __device__ __forceinline__ bool tail_visible(const LaneRow &L, const int *sh_blk
 }
 
 // ------------------------------------------------------------------------------------------------
-// bf16: LDS-DMA tiles, swizzled rows, transposing V reads
+// bf16: two wavefronts of 64 rows, LDS-DMA tiles, swizzled rows, transposing V reads
 // ------------------------------------------------------------------------------------------------
+// A workgroup is four wavefronts; each owns 32 of the item's 128 rows, two workgroups per CU (two
+// wavefronts per SIMD, whose MFMA and VALU phases interleave).
+constexpr int kBfThreads = 256;
+// Lazy rescale: a row's softmax reference moves only when a tile's maximum exceeds it by more than
+// kSlack (log2 units), so stored probabilities stay below 2^kSlack and the O rescale is rare.
+constexpr float kSlack = 8.f;
+
 // XOR swizzle of the 16-byte chunks of LDS row r. 256-byte rows (d = 128): chunk c of row r lives at
 // c ^ f(r) with f(r) = ((r & 3) << 2) | ((r >> 2) & 3) -- a bijection over any 16 aligned rows (the K
 // fragment reads: 16 rows, same chunk) that also puts the 4 aligned chunks of 4 consecutive rows in
 // distinct bank groups (the transposing V reads). 128-byte rows (d = 64) share a bank line in pairs:
-// f(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3) has the same two properties there.
+// f(r) = (((r >> 1) & 1) << 2) | ((r >> 2) & 3) has the same two properties there. f depends on
+// r mod 16 only.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D == 128)
@@ -314,83 +323,170 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int D>
 struct DmaTile {
-  static constexpr int RB = D * 2;                   // bytes per LDS row (one key, one head)
-  static constexpr int CH = D / 8;                   // 16-byte chunks per row
-  static constexpr int BYTES = kKeys * RB;           // one K or V tile
-  static constexpr int NI = BYTES / (kThreads * 16);  // DMA instructions per wavefront per tile
-  static constexpr int RPI = 64 / CH;                 // rows per DMA instruction
+  static constexpr int RB = D * 2;                      // bytes per LDS row (one key, one head)
+  static constexpr int CH = D / 8;                      // 16-byte chunks per row
+  static constexpr int BYTES = kKeys * RB;              // one K or V tile
+  static constexpr int NI = BYTES / (kBfThreads * 16);  // DMA instructions per wavefront per operand
+  static constexpr int RPI = 64 / CH;                   // rows per DMA instruction
 };
 
-// Copy rows 0..63 of one tile into `lds` (wave-uniform base). row_ptr(r) returns the global row of
-// tile key r; lane `lane` of instruction q fills LDS chunk q*64 + lane, i.e. row q*RPI + lane/CH,
-// physical chunk lane % CH, whose logical chunk is (lane % CH) ^ swz(row).
-template <int D, typename RF>
-__device__ __forceinline__ void dma_tile(char *lds, RF row_ptr) {
+// LDS byte offsets of this lane's fragments inside a tile, fixed for the whole walk.
+//  K (A operand of S^T = K Q^T), k-step kk: row col (+32 for the second 32-key half), chunk 2kk + hh.
+//  V^T (A operand of O^T = V^T P^T), k-step t, column block b: lane l gets column 32b + l%32 of keys
+//  16t + 4hh + {0..3} (first transposing read) and 16t + 8 + 4hh + {0..3} (second); inside its
+//  16-lane group, lane j points at row 16t + 4hh + j/4 (+8), columns 32b + 16((l>>4)&1) + 4(j%4).
+// Row bases are multiples of the row size and the swizzle acts on the chunk bits only, so the offset
+// of k-step kk is k ^ (kk << 5) and that of column block b is v ^ (b << 6); t moves by 16 rows, an
+// immediate. Three registers instead of one per fragment.
+template <int D>
+struct FragAddr {
+  uint32_t k, vlo, vhi;
+  __device__ __forceinline__ uint32_t kof(int kk) const { return k ^ static_cast<uint32_t>(kk << 5); }
+  __device__ __forceinline__ uint32_t vlof(int b) const { return vlo ^ static_cast<uint32_t>(b << 6); }
+  __device__ __forceinline__ uint32_t vhif(int b) const { return vhi ^ static_cast<uint32_t>(b << 6); }
+};
+
+template <int D>
+__device__ __forceinline__ FragAddr<D> frag_addr() {
   using TT = DmaTile<D>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < TT::NI; ++i) {
-    const int q = wave * TT::NI + i;
-    const int r = q * TT::RPI + lane / TT::CH;
-    const int c = (lane % TT::CH) ^ swz<D>(r);
-    const __bf16 *src = row_ptr(r) + c * 8;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src),
-                                     LDS_PTR(void, lds + q * 1024), 16, 0, 0);
-  }
+  const int lane = threadIdx.x & 63, col = lane & 31, hh = lane >> 5;
+  const int j = lane & 15, dd = (lane >> 4) & 1;
+  FragAddr<D> f;
+  f.k = col * TT::RB + ((hh ^ swz<D>(col)) << 4);
+  const int r1 = 4 * hh + (j >> 2), r2 = r1 + 8;
+  const int ch = 2 * dd + ((j & 3) >> 1), byte = (j & 1) * 8;
+  f.vlo = r1 * TT::RB + ((ch ^ swz<D>(r1)) << 4) + byte;
+  f.vhi = r2 * TT::RB + ((ch ^ swz<D>(r2)) << 4) + byte;
+  return f;
 }
 
-// One 64-key tile from LDS: S^T = K Q^T, softmax, O^T += V^T P^T.
-template <int D, typename VIS>
-__device__ __forceinline__ void tile_step_dma(const char *kst, const char *vst, const bf16x8 (&qf)[D / 16],
-                                              RowState<D> &st, float c, bool need_mask, VIS visible) {
+// DMA geometry of this lane: instruction i of wavefront w fills LDS bytes [(w*NI + i)*1024, +1024),
+// lane l the 16 bytes at l*16: row (w*NI + i)*RPI + l/CH, physical chunk l % CH, which holds the
+// row's logical chunk (l % CH) ^ swz(row). Recomputed where used (a few integer operations) rather
+// than held in registers for the whole walk.
+template <int D>
+__device__ __forceinline__ int dma_row(int i) {
   using TT = DmaTile<D>;
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 31, hh = lane >> 5;
+  return ((threadIdx.x >> 6) * TT::NI + i) * TT::RPI + (threadIdx.x & 63) / TT::CH;
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t dma_chunk(int i) {
+  return static_cast<uint32_t>((((threadIdx.x & 63) % DmaTile<D>::CH) ^ swz<D>(dma_row<D>(i))) << 4);
+}
+
+template <int D>
+__device__ __forceinline__ void dma16(const char *src, char *lds, int i) {
+  const int wave = threadIdx.x >> 6;
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src),
+                                   LDS_PTR(void, lds + (wave * DmaTile<D>::NI + i) * 1024), 16, 0, 0);
+}
+
+// The same copy through a buffer resource (base and byte range in SGPRs): the per-lane part of the
+// address is a 32-bit offset, the tile position a scalar offset, and bytes outside the range read
+// as zero.
+constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+template <int D>
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, char *lds, int i, uint32_t voff, uint32_t soff) {
+  const int wave = threadIdx.x >> 6;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, lds + (wave * DmaTile<D>::NI + i) * 1024), 16, voff,
+                                           soff, 0, 0);
+}
+
+template <int D>
+struct Rows1 {
+  f32x16 o[D / 32];
+  float m;  // softmax reference (scaled log2 units), -inf until a key is visible
+  float l;  // this lane's half of the running sum
+};
+
+// One 64-key tile: S^T = K Q^T, mask (MASK only), tile maximum and (rarely) the O rescale, then
+// P = 2^(c*S - m) as the bf16 B operand of O^T += V^T P^T. The lane holds the keys
+// kappa = mb*32 + 8*(r/4) + 4*hh + r%4 of its query column; visible(kappa - 4*hh) decides the mask
+// (the lane's 4*hh is folded into the caller's limit or table pointer, so the argument is a
+// compile-time constant). The row sum adds the bf16 values the PV product uses.
+template <int D, bool MASK, typename VIS>
+__device__ __forceinline__ void tile1(const char *kst, const char *vst, const FragAddr<D> &fa,
+                                      const bf16x8 (&q)[D / 16], Rows1<D> &st, float c, VIS visible) {
+  using TT = DmaTile<D>;
+  // The fragment reads are fenced into halves (scheduling barriers) so that at most half a tile of
+  // K or V fragments is in flight: the other wavefront of the SIMD covers the LDS latency.
   f32x16 s[2] = {};
-  bf16x8 kfr[2][D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
+  for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int row = mb * 32 + col;
-      kfr[mb][kk] = *reinterpret_cast<const bf16x8 *>(kst + row * TT::RB + (((2 * kk + hh) ^ swz<D>(row)) << 4));
-    }
+    for (int kk = h * D / 32; kk < (h + 1) * D / 32; ++kk)
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kst + fa.kof(kk) + 32 * mb * TT::RB);
+        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[kk], s[mb], 0, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (MASK) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[mb][kk], qf[kk], s[mb], 0, 0, 0);
-  softmax_update<D>(s, st, c, need_mask, visible);
-  // V^T fragment (t, b): lane l gets column d = 32b + l%32 of keys 16t + 4hh + {0..3} (first read)
-  // and 16t + 8 + 4hh + {0..3} (second read); in its 16-lane group, lane j points at row
-  // 16t + 4hh + j/4 (+8), columns 32b + 16*((l>>4)&1) + 4*(j%4) .. +3.
-  const int j = lane & 15, dd = (lane >> 4) & 1;
-  bf16x8 vfr[4][D / 32];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+      for (int r = 0; r < 16; ++r) {
+        s[mb][r] = visible(mb * 32 + 8 * (r >> 2) + (r & 3)) ? s[mb][r] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b) {
-      const int doff = 32 * b + 16 * dd + 4 * (j & 3);
-      const int ch = doff >> 3, byte = (doff & 7) * 2;
-      const int r1 = 16 * t + 4 * hh + (j >> 2), r2 = r1 + 8;
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(v4i16, vst + r1 * TT::RB + ((ch ^ swz<D>(r1)) << 4) + byte));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          LDS_PTR(v4i16, vst + r2 * TT::RB + ((ch ^ swz<D>(r2)) << 4) + byte));
-      const v4i16 both[2] = {lo, hi};
-      vfr[t][b] = *reinterpret_cast<const bf16x8 *>(both);
-    }
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mt = mx * c;
+  const bool up = mt > st.m + kSlack;  // m = -inf: any finite maximum moves it
+  if (__ballot(up)) {
+    const float mn = up ? mt : st.m;
+    const float al = up ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;
+    st.l *= al;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[b][r] *= al;
+    st.m = mn;
+  }
+  const float mu = st.m == -INFINITY ? 0.f : st.m;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  bf16x8 p[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    bf16x8 pb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[t >> 1][8 * (t & 1) + i]);
+    for (int i = 0; i < 8; ++i)
+      p[t][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + i], c, -mu)));
 #pragma unroll
-    for (int b = 0; b < D / 32; ++b) st.o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[t][b], pb, st.o[b], 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+      const bf16x2 pr = {p[t][2 * u], p[t][2 * u + 1]};
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.l, false);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 2 * h; t < 2 * h + 2; ++t)
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b) {
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vst + fa.vlof(b) + 16 * t * TT::RB));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vst + fa.vhif(b) + 16 * t * TT::RB));
+        const v4i16 both[2] = {lo, hi};
+        st.o[b] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(both), p[t], st.o[b], 0, 0, 0);
+      }
   }
 }
 
-template <int D, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel_bf16(const AttnArgs a) {
+// Key / value source of the bf16 walk: a contiguous per-request cache, a paged cache whose page size
+// is a multiple of the rows one DMA instruction covers (page id wave-uniform), or any paged cache.
+enum KvMode { kContig = 0, kPagedWave = 1, kPagedLane = 2 };
+
+template <int D, int KV>
+__global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs a) {
   using TT = DmaTile<D>;
   // one LDS object per stage and operand, so that the DMA into one stage is provably independent of
   // the reads of the other (no conservative wait between them)
@@ -404,85 +500,165 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel_bf16(const AttnArgs a
   Item it;
   if (!decode_item(a, it)) return;
   const ReqInfo &R = it.R;
-  const LaneRow L = lane_row(a, it);
-  const int hh = (threadIdx.x & 63) >> 5;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5;
+  // this lane's query row (recomputed after the walk instead of held in registers)
+  auto row_of = [&]() __attribute__((always_inline)) { return lane_row(a, it, wave * 32 + (lane & 31)); };
   bf16x8 qf[D / 16];
   {
-    const __bf16 *qrow = static_cast<const __bf16 *>(a.q) + (static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h) * D;
+    const LaneRow L = row_of();
+    const __bf16 *qrow =
+        static_cast<const __bf16 *>(a.q) + (static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = L.valid ? *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8) : bf16x8{};
   }
-  RowState<D> st;
+  Rows1<D> st;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) st.o[b] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
   const float c = a.scale_log2;
+  const FragAddr<D> fa = frag_addr<D>();
+  const size_t row_bytes = static_cast<size_t>(a.Hkv) * D * 2;  // bytes between consecutive tokens
 
-  // ---- prefix phase ----
+  // ---- prefix phase: double-buffered 64-key tiles, one barrier per tile ----
   if (it.k1 > it.k0) {
-    const size_t rs = static_cast<size_t>(a.Hkv) * D;
-    const __bf16 *kc = static_cast<const __bf16 *>(a.k_cache);
-    const __bf16 *vc = static_cast<const __bf16 *>(a.v_cache);
-    const __bf16 *kb = kc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D;
-    const __bf16 *vb = vc + (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D;
     const int k1 = it.k1;
-    // global row of prefix token jj, clamped to the last token of this split's range (keys past the
-    // end are masked, so only their address matters)
-    auto row_at = [&](const __bf16 *flat, const __bf16 *cache, int jj) -> const __bf16 * {
-      jj = min(jj, k1 - 1);
-      if (!PAGED) return flat + jj * rs;
-      int page = a.page_table[static_cast<size_t>(R.req) * a.max_pages + jj / a.page_size];
-      page = min(max(page, 0), a.num_pages - 1);
-      return cache + ((static_cast<size_t>(page) * a.page_size + (jj % a.page_size)) * a.Hkv + it.g) * D;
+    const char *kc = static_cast<const char *>(a.k_cache);
+    const char *vc = static_cast<const char *>(a.v_cache);
+    // Paged caches: with page_size a multiple of RPI every DMA instruction reads RPI consecutive
+    // tokens of one page, so its page id is wave-uniform (a scalar load, one tile ahead) and the
+    // address is a scalar page base plus a 32-bit lane offset. Other page sizes take a per-lane path.
+    constexpr bool PAGED = KV != kContig;
+    constexpr bool page_uniform = KV == kPagedWave;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int pg[TT::NI];  // page ids of the tile whose DMA is issued next
+    auto load_pages = [&](int kt) __attribute__((always_inline)) {
+      if constexpr (PAGED) {
+        const int32_t *pt = a.page_table + static_cast<size_t>(R.req) * a.max_pages;
+        if constexpr (page_uniform) {
+#pragma unroll
+          for (int i = 0; i < TT::NI; ++i)
+            pg[i] = pt[min(kt + (wave_u * TT::NI + i) * TT::RPI, k1 - 1) / a.page_size];
+        } else {
+#pragma unroll
+          for (int i = 0; i < TT::NI; ++i) pg[i] = pt[min(kt + dma_row<D>(i), k1 - 1) / a.page_size];
+        }
+      }
     };
-    auto issue = [&](char *kdst, char *vdst, int kt) {
-      dma_tile<D>(kdst, [&](int r) { return row_at(kb, kc, kt + r); });
-      dma_tile<D>(vdst, [&](int r) { return row_at(vb, vc, kt + r); });
+    // contiguous cache: this request's key / value rows of head g as buffers; rows of the last tile
+    // past the split's end are masked, and past the request's rows they read as zero
+    uint32_t off[TT::NI];  // byte offsets of this lane's 16-byte pieces in a tile
+    __amdgpu_buffer_rsrc_t krs, vrs;
+    if constexpr (!PAGED) {
+#pragma unroll
+      for (int i = 0; i < TT::NI; ++i) off[i] = static_cast<uint32_t>(dma_row<D>(i) * row_bytes) + dma_chunk<D>(i);
+      const size_t base = (static_cast<size_t>(R.req) * a.kv_stride * a.Hkv + it.g) * D * 2;
+      const int range = static_cast<int>(static_cast<size_t>(a.kv_stride) * row_bytes - static_cast<size_t>(it.g) * D * 2);
+      krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kc + base), 0, range, kBufWord3);
+      vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vc + base), 0, range, kBufWord3);
+    }
+    // DMA of the K and V tile at prefix token kt into kd / vd
+    auto issue = [&](char *kd, char *vd, int kt) __attribute__((always_inline)) {
+      if constexpr (PAGED) {
+        const size_t page_bytes = static_cast<size_t>(a.page_size) * row_bytes;
+        if constexpr (page_uniform) {
+          const int lr = (lane & 63) / TT::CH;  // row inside the instruction's RPI rows
+#pragma unroll
+          for (int i = 0; i < TT::NI; ++i) {
+            const int jj0 = min(kt + (wave_u * TT::NI + i) * TT::RPI, k1 - 1);
+            const int page = min(max(pg[i], 0), a.num_pages - 1);
+            const int rip = min(jj0 % a.page_size + lr, a.page_size - 1);  // stays in the page; masked past k1
+            const size_t pbase = static_cast<size_t>(page) * page_bytes + static_cast<size_t>(it.g) * D * 2;
+            const uint32_t lo = static_cast<uint32_t>(rip * row_bytes) + dma_chunk<D>(i);
+            dma16<D>(kc + pbase + lo, kd, i);
+            dma16<D>(vc + pbase + lo, vd, i);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < TT::NI; ++i) {
+            const int jj = min(kt + dma_row<D>(i), k1 - 1);
+            const int page = min(max(pg[i], 0), a.num_pages - 1);
+            const size_t o = ((static_cast<size_t>(page) * a.page_size + (jj % a.page_size)) * a.Hkv + it.g) * D * 2 +
+                             dma_chunk<D>(i);
+            dma16<D>(kc + o, kd, i);
+            dma16<D>(vc + o, vd, i);
+          }
+        }
+      } else {
+        const uint32_t soff = static_cast<uint32_t>(kt * row_bytes);
+#pragma unroll
+        for (int i = 0; i < TT::NI; ++i) {
+          dma16_buf<D>(krs, kd, i, off[i], soff);
+          dma16_buf<D>(vrs, vd, i, off[i], soff);
+        }
+      }
     };
-    // one tile: prefetch the next into the other stage, compute this one, then wait for the
-    // prefetch (own DMA) and for every wavefront (barrier)
-    auto body = [&](const char *kcur, const char *vcur, char *knext, char *vnext, int kt) {
-      if (kt + kKeys < k1) issue(knext, vnext, kt + kKeys);
-      const int lim = k1 - kt;
-      tile_step_dma<D>(kcur, vcur, qf, st, c, lim < kKeys, [&](int key) { return key < lim; });
+    // Full tiles in a loop unrolled over the two stages; the ragged last tile (if any) after it, so
+    // that no tile variant joins the loop's accumulators. Each step prefetches the next tile into
+    // the other stage, computes this one, then waits for its own DMA and for every wavefront.
+    const int n_full = (k1 - it.k0) / kKeys;
+    const int n_tiles = (k1 - it.k0 + kKeys - 1) / kKeys;
+    auto prefetch = [&](char *knext, char *vnext, int i) __attribute__((always_inline)) {
+      if (i + 1 < n_tiles) {
+        issue(knext, vnext, it.k0 + (i + 1) * kKeys);
+        if (i + 2 < n_tiles) load_pages(it.k0 + (i + 2) * kKeys);
+      }
+    };
+    auto body = [&](const char *kcur, const char *vcur, char *knext, char *vnext, int i)
+                    __attribute__((always_inline)) {
+      prefetch(knext, vnext, i);
+      tile1<D, false>(kcur, vcur, fa, qf, st, c, [](int) { return true; });
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     };
+    load_pages(it.k0);
     issue(lds_k0, lds_v0, it.k0);
+    if (n_tiles > 1) load_pages(it.k0 + kKeys);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = it.k0; kt < k1; kt += 2 * kKeys) {
-      body(lds_k0, lds_v0, lds_k1, lds_v1, kt);
-      if (kt + kKeys < k1) body(lds_k1, lds_v1, lds_k0, lds_v0, kt + kKeys);
+    for (int i = 0; i < n_full; i += 2) {
+      body(lds_k0, lds_v0, lds_k1, lds_v1, i);
+      if (i + 1 < n_full) body(lds_k1, lds_v1, lds_k0, lds_v0, i + 1);
+    }
+    if (n_full < n_tiles) {  // ragged last tile: keys past the split's end are masked
+      const int lim_hh = k1 - (it.k0 + n_full * kKeys) - 4 * hh;
+      if (n_full & 1)
+        tile1<D, true>(lds_k1, lds_v1, fa, qf, st, c, [&](int kc) { return kc < lim_hh; });
+      else
+        tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c, [&](int kc) { return kc < lim_hh; });
+      __syncthreads();
     }
   }
 
   // ---- in-pack tail (first split only) ----
   if (it.split == 0) {
+    const LaneRow L = row_of();
     const TailList tl = tail_list(a, it);
-    const __bf16 *kn = static_cast<const __bf16 *>(a.k_new);
-    const __bf16 *vn = static_cast<const __bf16 *>(a.v_new);
+    const size_t gb = static_cast<size_t>(it.g) * D * 2;
+    const int range = static_cast<int>(static_cast<size_t>(a.n_new) * row_bytes - gb);
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(a.k_new) + gb), 0, range, kBufWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(a.v_new) + gb), 0, range, kBufWord3);
     for (int kt = 0; kt < tl.n; kt += kKeys) {
       __syncthreads();
       tail_tables(a, tl, kt, sh_row, sh_blk, sh_pos);
       __syncthreads();
-      auto src = [&](const __bf16 *base) {
-        return [&, base](int r) -> const __bf16 * {
-          const int rr = max(sh_row[r], 0);  // unused slots read row 0 of the request; masked
-          return base + (static_cast<size_t>(R.q_begin + rr) * a.Hkv + it.g) * D;
-        };
-      };
-      dma_tile<D>(lds_k0, src(kn));
-      dma_tile<D>(lds_v0, src(vn));
+#pragma unroll
+      for (int i = 0; i < TT::NI; ++i) {
+        const int rr = max(sh_row[dma_row<D>(i)], 0);  // unused slots read row 0 of the request; masked
+        const uint32_t o = static_cast<uint32_t>((R.q_begin + rr) * row_bytes) + dma_chunk<D>(i);
+        dma16_buf<D>(krs, lds_k0, i, o, 0);
+        dma16_buf<D>(vrs, lds_v0, i, o, 0);
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      tile_step_dma<D>(lds_k0, lds_v0, qf, st, c, true,
-                       [&](int key) { return tail_visible(L, sh_blk, sh_pos, key); });
+      tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c,
+                     [&](int kc) { return tail_visible(L, sh_blk + 4 * hh, sh_pos + 4 * hh, kc); });
     }
   }
-  write_result<__bf16, D>(a, it, L, st);
+  write_result<__bf16, D>(a, it, row_of(), st.o, st.m, st.l);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -560,7 +736,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel_f32(const AttnArgs a)
   Item it;
   if (!decode_item(a, it)) return;
   const ReqInfo &R = it.R;
-  const LaneRow L = lane_row(a, it);
+  const LaneRow L = lane_row(a, it, (threadIdx.x >> 6) * 32 + (threadIdx.x & 31));
   const int hh = (threadIdx.x & 63) >> 5;
   float qf[D / 2];
   {
@@ -619,7 +795,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel_f32(const AttnArgs a)
       tile_step_f32<D>(ks, vs, qf, st, c, true, [&](int key) { return tail_visible(L, sh_blk, sh_pos, key); });
     }
   }
-  write_result<float, D>(a, it, L, st);
+  write_result<float, D>(a, it, L, st.o, st.m, st.l);
 }
 
 // Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. Each thread owns four
@@ -691,7 +867,8 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
     if (off[i + 1] < off[i] || pre[i] < 0) return D3D_EINVAL;
   }
   const long long total_q = static_cast<long long>(off[n_req]) * B;
-  if (total_q >= (1ll << 31)) return D3D_EUNSUPPORTED;
+  // packed rows are addressed with 32-bit byte offsets (buffer loads)
+  if (total_q * Hkv * D * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;
   const int Qt = kRows / G;
   AttnArgs &a = P->args;
   a.B = B;
@@ -699,6 +876,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   a.Hkv = Hkv;
   a.G = G;
   a.Qt = Qt;
+  a.n_new = static_cast<int>(total_q);
 
   std::vector<int> n_q(n_req), tiles(n_req), splits(n_req), len(n_req);
   long long base_items = 0;
@@ -772,10 +950,13 @@ template <typename T, int D>
 void launch(const AttnPlan &P, bool paged, hipStream_t stream) {
   if (P.args.n_groups > 0) {
     if constexpr (Cfg<T>::kBf16) {
-      if (paged)
-        attn_kernel_bf16<D, true><<<P.grid, kThreads, 0, stream>>>(P.args);
+      // rows one DMA instruction covers: 64 / (D / 8)
+      if (!paged)
+        attn_kernel_bf16<D, kContig><<<P.grid, kBfThreads, 0, stream>>>(P.args);
+      else if (P.args.page_size % (512 / D) == 0)
+        attn_kernel_bf16<D, kPagedWave><<<P.grid, kBfThreads, 0, stream>>>(P.args);
       else
-        attn_kernel_bf16<D, false><<<P.grid, kThreads, 0, stream>>>(P.args);
+        attn_kernel_bf16<D, kPagedLane><<<P.grid, kBfThreads, 0, stream>>>(P.args);
     } else {
       if (paged)
         attn_kernel_f32<D, true><<<P.grid, kThreads, 0, stream>>>(P.args);
@@ -820,8 +1001,10 @@ extern "C" int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_n
   if (paged) {
     if (page_size < 1 || max_pages < 1 || num_pages < 1) return D3D_EINVAL;
     if (static_cast<long long>(max_pages) * page_size < max_pre) return D3D_EINVAL;
-  } else if (max_pre > 0 && kv_stride < max_pre) {
-    return D3D_EINVAL;
+  } else if (max_pre > 0) {
+    if (kv_stride < max_pre) return D3D_EINVAL;
+    // one request's rows of the contiguous cache are addressed with 32-bit byte offsets
+    if (static_cast<long long>(kv_stride) * n_heads_kv * head_dim * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;
   }
   if (P.ws_bytes && (!ws || ws_bytes < P.ws_bytes)) return D3D_EWORKSPACE;
   for (const void *ptr : {q, k_new, v_new, static_cast<const void *>(out)})

@@ -159,3 +159,21 @@ def test_paged_small_ragged_pages():
                k_prefix=[mk(L, 2, 64) for L in lens], v_prefix=[mk(L, 2, 64) for L in lens])
     prob = AttnProblem("bf16", B, reqs, inp, paged=True, page_size=16, seed=3)
     _check(prob, None, "paged-small")
+
+
+@pytest.mark.parametrize("page_size,d", [(8, 64), (4, 128), (32, 128), (5, 128), (3, 64), (1, 128)])
+def test_paged_page_sizes(page_size, d):
+    """Page sizes that are multiples of the rows one 16-byte-per-lane copy instruction covers
+    (4 at d = 128, 8 at d = 64) take the wave-uniform page path; the others (5, 3, 1) the per-lane
+    path. Prefix lengths straddle page and tile boundaries."""
+    require_gpu()
+    _say(f"attention: paged, page_size {page_size}, d {d}")
+    rng = np.random.default_rng(100 + page_size + d)
+    B, lens = 16, [70, 129, 3, 300]
+    reqs = [dict(L=L, kind="async", C=3, F=2) for L in lens]
+    tot = len(lens) * 6 * B
+    mk = lambda *s: synth.round_bf16(rng.standard_normal(s).astype(np.float32))
+    inp = dict(q=mk(tot, 8, d), k_new=mk(tot, 2, d), v_new=mk(tot, 2, d),
+               k_prefix=[mk(L, 2, d) for L in lens], v_prefix=[mk(L, 2, d) for L in lens])
+    prob = AttnProblem("bf16", B, reqs, inp, paged=True, page_size=page_size, seed=page_size)
+    _check(prob, None, f"paged-ps{page_size}-d{d}")
