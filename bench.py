@@ -97,7 +97,7 @@ class Round:
         self.descs = torch.empty((n_blk, 4), dtype=torch.int32, device="cuda")
         self.off_dev = torch.from_numpy(self.off).cuda()
         self.out = torch.empty_like(self.q)
-        need = _binding.draft_attn_packed_workspace(self.off, self.lens, self.B, self.q.shape[1],
+        need = _binding.draft_attn_packed_workspace(self.q.dtype, self.off, self.lens, self.B, self.q.shape[1],
                                                     self.k_new.shape[1], self.q.shape[2])
         self.attn_ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
         nd = self.B - 1

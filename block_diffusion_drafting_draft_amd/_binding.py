@@ -25,8 +25,8 @@ _i32p = _c.POINTER(_c.c_int32)
 _SIGNATURES = {
     "d3d_build_branch_descs": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int32, _i32p,
                                            _c.c_void_p, _c.c_int, _c.POINTER(_c.c_int)]),
-    "draft_attn_packed_workspace": (_c.c_size_t, [_i32p, _i32p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
-                                                  _c.c_int]),
+    "draft_attn_packed_workspace": (_c.c_size_t, [_c.c_int, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int,
+                                                  _c.c_int, _c.c_int]),
     "draft_attn_packed": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                      _c.c_void_p, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -82,11 +82,17 @@ def _stream(stream):
 
 
 def _dtype_code(t):
-    if t.dtype == torch.bfloat16:
+    """d3d_dtype of a tensor, a torch dtype, "bf16" / "f32", or an existing code."""
+    if isinstance(t, int):
+        if t in (D3D_BF16, D3D_F32):
+            return t
+        raise TypeError(f"unsupported dtype code {t}")
+    dt = t.dtype if hasattr(t, "dtype") else t
+    if dt in (torch.bfloat16, "bf16"):
         return D3D_BF16
-    if t.dtype == torch.float32:
+    if dt in (torch.float32, "f32"):
         return D3D_F32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TypeError(f"unsupported dtype {dt}")
 
 
 def _dev(t, name):
@@ -108,11 +114,14 @@ def d3d_build_branch_descs(block_size, coverage, fanout, prefix_len, cur_anchor,
     return out[:n.value]
 
 
-def draft_attn_packed_workspace(req_block_off, req_prefix_len, block_size, n_heads_q, n_heads_kv, head_dim):
+def draft_attn_packed_workspace(dtype, req_block_off, req_prefix_len, block_size, n_heads_q, n_heads_kv,
+                                head_dim):
+    """Workspace bytes for draft_attn_packed on the current device; dtype is torch.bfloat16 /
+    torch.float32 or "bf16" / "f32"."""
     off, off_p = _host_i32(req_block_off)
     pre, pre_p = _host_i32(req_prefix_len)
-    return int(load().draft_attn_packed_workspace(off_p, pre_p, len(pre), block_size, n_heads_q, n_heads_kv,
-                                                  head_dim))
+    return int(load().draft_attn_packed_workspace(_dtype_code(dtype), off_p, pre_p, len(pre), block_size, n_heads_q,
+                                                  n_heads_kv, head_dim))
 
 
 def draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, req_prefix_len, block_size,
@@ -161,7 +170,7 @@ def draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, r
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out")
-    need = draft_attn_packed_workspace(off, pre, block_size, hq, hkv, d)
+    need = draft_attn_packed_workspace(dt, off, pre, block_size, hq, hkv, d)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     scale = d ** -0.5 if scale is None else scale

@@ -40,10 +40,10 @@
 namespace d3d {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;  // query-head rows per workgroup
-constexpr int kKeys = 64;   // keys per tile
-constexpr int kTargetItems = 768;
+constexpr int kThreads = 256;  // fp32 kernel and the split combine
+constexpr int kRows = 128;     // query-head rows per fp32 work item
+constexpr int kBfRows = 256;   // query-head rows per bf16 work item
+constexpr int kKeys = 64;      // keys per tile
 constexpr int kMinSplit = 256;
 constexpr int kMaxSplits = 16;
 
@@ -300,9 +300,11 @@ __device__ __forceinline__ bool tail_visible(const LaneRow &L, const int *sh_blk
 // ------------------------------------------------------------------------------------------------
 // bf16: two wavefronts of 64 rows, LDS-DMA tiles, swizzled rows, transposing V reads
 // ------------------------------------------------------------------------------------------------
-// A workgroup is four wavefronts; each owns 32 of the item's 128 rows, two workgroups per CU (two
-// wavefronts per SIMD, whose MFMA and VALU phases interleave).
-constexpr int kBfThreads = 256;
+// A workgroup is eight wavefronts, one per CU; each wavefront owns 32 of the item's 256 rows (two
+// wavefronts per SIMD, whose MFMA and VALU phases interleave). Every K/V tile in LDS serves all 256
+// rows, and a ring of four tiles keeps three copies in flight ahead of the one being computed.
+constexpr int kBfThreads = 512;
+constexpr int kStages = 4;
 // Lazy rescale: a row's softmax reference moves only when a tile's maximum exceeds it by more than
 // kSlack (log2 units), so stored probabilities stay below 2^kSlack and the O rescale is rare.
 constexpr float kSlack = 8.f;
@@ -375,24 +377,55 @@ __device__ __forceinline__ uint32_t dma_chunk(int i) {
   return static_cast<uint32_t>((((threadIdx.x & 63) % DmaTile<D>::CH) ^ swz<D>(dma_row<D>(i))) << 4);
 }
 
+// The copies into LDS are issued as inline assembly: the compiler then does not see them as LDS
+// writes, so it neither tracks nor waits for them before LDS reads (its tracking is per LDS object
+// and limited, and a lost track costs a wait for every copy in flight). Completion is handled
+// explicitly: wait_vm before the barrier that publishes a stage, and a full wait before reuse.
+// Vector-memory operations complete in issue order, so extra younger operations only make the
+// compiler's own vmcnt waits stricter. m0 holds the wavefront's LDS destination (an asm input).
 template <int D>
-__device__ __forceinline__ void dma16(const char *src, char *lds, int i) {
-  const int wave = threadIdx.x >> 6;
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src),
-                                   LDS_PTR(void, lds + (wave * DmaTile<D>::NI + i) * 1024), 16, 0, 0);
+__device__ __forceinline__ uint32_t lds_dst(char *lds, int i) {
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, lds))) + (wave * DmaTile<D>::NI + i) * 1024;
 }
 
-// The same copy through a buffer resource (base and byte range in SGPRs): the per-lane part of the
-// address is a 32-bit offset, the tile position a scalar offset, and bytes outside the range read
-// as zero.
+// 16 bytes per lane from a 64-bit per-lane address.
+template <int D>
+__device__ __forceinline__ void dma16(const char *src, char *lds, int i) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_dst<D>(lds, i)) : "memory");
+}
+
+// 16 bytes per lane from a wave-uniform base plus a 32-bit lane offset.
+template <int D>
+__device__ __forceinline__ void dma16_s(const char *base, uint32_t voff, char *lds, int i) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_dst<D>(lds, i)) : "memory");
+}
+
+// The same through a buffer resource (base and byte range in SGPRs): the tile position is a scalar
+// offset, and bytes outside the range read as zero.
 constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 template <int D>
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rsrc, char *lds, int i, uint32_t voff, uint32_t soff) {
-  const int wave = threadIdx.x >> 6;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(void, lds + (wave * DmaTile<D>::NI + i) * 1024), 16, voff,
-                                           soff, 0, 0);
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+               "{m0}"(lds_dst<D>(lds, i))
+               : "memory");
 }
+
+// Wait until at most N vector-memory operations of this wavefront are outstanding (the copies of
+// later tiles may stay in flight). Other counters are not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a memory fence: __syncthreads() releases at workgroup scope, which waits
+// for every outstanding vector-memory operation (vmcnt(0)) and would drain the copies of later
+// tiles. The copy the next step reads has been waited for explicitly (wait_vm), this wavefront's LDS
+// reads are complete (lgkmcnt(0)), and the memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void barrier_keep_copies() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D>
 struct Rows1 {
@@ -489,11 +522,17 @@ template <int D, int KV>
 __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs a) {
   using TT = DmaTile<D>;
   // one LDS object per stage and operand, so that the DMA into one stage is provably independent of
-  // the reads of the other (no conservative wait between them)
-  __shared__ __attribute__((aligned(1024))) char lds_k0[TT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[TT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[TT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[TT::BYTES];
+  // the reads of the others (no conservative wait between them)
+  // (K tile then V tile per stage: four objects, few enough for the compiler to track each stage's
+  // copies separately)
+  __shared__ __attribute__((aligned(1024))) char lds_s0[2 * TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_s1[2 * TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_s2[2 * TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_s3[2 * TT::BYTES];
+  char *const lds_k0 = lds_s0, *const lds_v0 = lds_s0 + TT::BYTES;
+  char *const lds_k1 = lds_s1, *const lds_v1 = lds_s1 + TT::BYTES;
+  char *const lds_k2 = lds_s2, *const lds_v2 = lds_s2 + TT::BYTES;
+  char *const lds_k3 = lds_s3, *const lds_v3 = lds_s3 + TT::BYTES;
   __shared__ int sh_row[kKeys];
   __shared__ int sh_blk[kKeys];
   __shared__ int sh_pos[kKeys];
@@ -512,6 +551,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = L.valid ? *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8) : bf16x8{};
   }
+  // Q has landed before the walk (a wait the compiler sees: otherwise it keeps Q pending into the
+  // loop and waits there for every copy in flight)
+  __builtin_amdgcn_s_waitcnt(0);
   Rows1<D> st;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) st.o[b] = f32x16{};
@@ -521,7 +563,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
   const FragAddr<D> fa = frag_addr<D>();
   const size_t row_bytes = static_cast<size_t>(a.Hkv) * D * 2;  // bytes between consecutive tokens
 
-  // ---- prefix phase: double-buffered 64-key tiles, one barrier per tile ----
+  // ---- prefix phase: 64-key tiles through a four-stage ring, one barrier per tile ----
   if (it.k1 > it.k0) {
     const int k1 = it.k1;
     const char *kc = static_cast<const char *>(a.k_cache);
@@ -537,9 +579,12 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
       if constexpr (PAGED) {
         const int32_t *pt = a.page_table + static_cast<size_t>(R.req) * a.max_pages;
         if constexpr (page_uniform) {
+          // the page table is read-only during the kernel: constant-space loads with a wave-uniform
+          // index become scalar loads
+          const __attribute__((address_space(4))) int32_t *ptc = (const __attribute__((address_space(4))) int32_t *)pt;
 #pragma unroll
           for (int i = 0; i < TT::NI; ++i)
-            pg[i] = pt[min(kt + (wave_u * TT::NI + i) * TT::RPI, k1 - 1) / a.page_size];
+            pg[i] = ptc[min(kt + (wave_u * TT::NI + i) * TT::RPI, k1 - 1) / a.page_size];
         } else {
 #pragma unroll
           for (int i = 0; i < TT::NI; ++i) pg[i] = pt[min(kt + dma_row<D>(i), k1 - 1) / a.page_size];
@@ -571,8 +616,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
             const int rip = min(jj0 % a.page_size + lr, a.page_size - 1);  // stays in the page; masked past k1
             const size_t pbase = static_cast<size_t>(page) * page_bytes + static_cast<size_t>(it.g) * D * 2;
             const uint32_t lo = static_cast<uint32_t>(rip * row_bytes) + dma_chunk<D>(i);
-            dma16<D>(kc + pbase + lo, kd, i);
-            dma16<D>(vc + pbase + lo, vd, i);
+            dma16_s<D>(kc + pbase, lo, kd, i);
+            dma16_s<D>(vc + pbase, lo, vd, i);
           }
         } else {
 #pragma unroll
@@ -594,39 +639,57 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
         }
       }
     };
-    // Full tiles in a loop unrolled over the two stages; the ragged last tile (if any) after it, so
-    // that no tile variant joins the loop's accumulators. Each step prefetches the next tile into
-    // the other stage, computes this one, then waits for its own DMA and for every wavefront.
+    // Full tiles in a loop unrolled over the four stages; the ragged last tile (if any) after it, so
+    // that no tile variant joins the loop's accumulators. Step i prefetches tile i+3 into the stage
+    // read at step i-1, computes tile i, then waits for its own copy of tile i+1 (the copies of
+    // tiles i+2, i+3 may stay in flight) and for every wavefront.
     const int n_full = (k1 - it.k0) / kKeys;
     const int n_tiles = (k1 - it.k0 + kKeys - 1) / kKeys;
-    auto prefetch = [&](char *knext, char *vnext, int i) __attribute__((always_inline)) {
-      if (i + 1 < n_tiles) {
-        issue(knext, vnext, it.k0 + (i + 1) * kKeys);
-        if (i + 2 < n_tiles) load_pages(it.k0 + (i + 2) * kKeys);
-      }
+    auto wait_next = [&](int i) __attribute__((always_inline)) {
+      const int later = n_tiles - i - 2;  // tiles issued after tile i+1 (at most two)
+      if (later >= 2)
+        wait_vm<4 * TT::NI>();
+      else if (later == 1)
+        wait_vm<2 * TT::NI>();
+      else
+        wait_vm<0>();
+      barrier_keep_copies();
     };
-    auto body = [&](const char *kcur, const char *vcur, char *knext, char *vnext, int i)
-                    __attribute__((always_inline)) {
-      prefetch(knext, vnext, i);
+    auto body = [&](const char *kcur, const char *vcur, char *kpre, char *vpre, int i) __attribute__((always_inline)) {
+      if (i + 3 < n_tiles) {
+        issue(kpre, vpre, it.k0 + (i + 3) * kKeys);
+        if (i + 4 < n_tiles) load_pages(it.k0 + (i + 4) * kKeys);
+      }
       tile1<D, false>(kcur, vcur, fa, qf, st, c, [](int) { return true; });
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      wait_next(i);
     };
     load_pages(it.k0);
     issue(lds_k0, lds_v0, it.k0);
-    if (n_tiles > 1) load_pages(it.k0 + kKeys);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int i = 0; i < n_full; i += 2) {
-      body(lds_k0, lds_v0, lds_k1, lds_v1, i);
+    if (n_tiles > 1) {
+      load_pages(it.k0 + kKeys);
+      issue(lds_k1, lds_v1, it.k0 + kKeys);
+    }
+    if (n_tiles > 2) {
+      load_pages(it.k0 + 2 * kKeys);
+      issue(lds_k2, lds_v2, it.k0 + 2 * kKeys);
+    }
+    if (n_tiles > 3) load_pages(it.k0 + 3 * kKeys);
+    wait_next(-1);
+    for (int i = 0; i < n_full; i += kStages) {
+      body(lds_k0, lds_v0, lds_k3, lds_v3, i);
       if (i + 1 < n_full) body(lds_k1, lds_v1, lds_k0, lds_v0, i + 1);
+      if (i + 2 < n_full) body(lds_k2, lds_v2, lds_k1, lds_v1, i + 2);
+      if (i + 3 < n_full) body(lds_k3, lds_v3, lds_k2, lds_v2, i + 3);
     }
     if (n_full < n_tiles) {  // ragged last tile: keys past the split's end are masked
       const int lim_hh = k1 - (it.k0 + n_full * kKeys) - 4 * hh;
-      if (n_full & 1)
-        tile1<D, true>(lds_k1, lds_v1, fa, qf, st, c, [&](int kc) { return kc < lim_hh; });
-      else
-        tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c, [&](int kc) { return kc < lim_hh; });
+      auto vis = [&](int kc) { return kc < lim_hh; };
+      switch (n_full % kStages) {
+        case 0: tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c, vis); break;
+        case 1: tile1<D, true>(lds_k1, lds_v1, fa, qf, st, c, vis); break;
+        case 2: tile1<D, true>(lds_k2, lds_v2, fa, qf, st, c, vis); break;
+        default: tile1<D, true>(lds_k3, lds_v3, fa, qf, st, c, vis); break;
+      }
       __syncthreads();
     }
   }
@@ -652,7 +715,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
         dma16_buf<D>(krs, lds_k0, i, o, 0);
         dma16_buf<D>(vrs, lds_v0, i, o, 0);
       }
-      __builtin_amdgcn_s_waitcnt(0);
+      wait_vm<0>();
       __syncthreads();
       tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c,
                      [&](int kc) { return tail_visible(L, sh_blk + 4 * hh, sh_pos + 4 * hh, kc); });
@@ -855,8 +918,26 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
-int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, int Hkv, int D,
-              AttnPlan *P) {
+// Compute units of the current device (one bf16 / fp32 workgroup each); 256 when no device answers.
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n < 1) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
+
+// Work items are (request, row tile of `rows` query-head rows, key/value head); a request's prefix
+// may be cut into s equal key ranges ("splits") so that there are enough items for every compute
+// unit, at the price of partial results that a second pass merges. The split count is the one that
+// minimises a simple estimate, in microseconds, of
+//   makespan: max(longest item, ceil(items / slots) * mean item), items of 64-key tiles at an
+//             assumed ~50 % of the MFMA rate, and
+//   merge:    the partial rows written and read back once at an assumed ~5 TB/s.
+int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, int Hkv, int D, int rows,
+              int slots, AttnPlan *P) {
   if (!off || !pre || n_req < 1 || n_req > D3D_ATTN_MAX_REQ) return D3D_EINVAL;
   if (B < 1 || B > 64 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return D3D_EINVAL;
   const int G = Hq / Hkv;
@@ -869,7 +950,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   const long long total_q = static_cast<long long>(off[n_req]) * B;
   // packed rows are addressed with 32-bit byte offsets (buffer loads)
   if (total_q * Hkv * D * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;
-  const int Qt = kRows / G;
+  const int Qt = rows / G;
   AttnArgs &a = P->args;
   a.B = B;
   a.Hq = Hq;
@@ -879,23 +960,44 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   a.n_new = static_cast<int>(total_q);
 
   std::vector<int> n_q(n_req), tiles(n_req), splits(n_req), len(n_req);
-  long long base_items = 0;
   for (int i = 0; i < n_req; ++i) {
     n_q[i] = (off[i + 1] - off[i]) * B;
     tiles[i] = (n_q[i] + Qt - 1) / Qt;
-    base_items += static_cast<long long>(tiles[i]) * Hkv;
   }
-  const long long factor = base_items >= kTargetItems || base_items == 0
-                               ? 1
-                               : (kTargetItems + base_items - 1) / base_items;
+  const double tile_us = kKeys * static_cast<double>(rows) * D * 4 / 4.9e12 * 1e6;
+  const double row_us = (D * 4.0 + 8.0) * 2 / 5e12 * 1e6;
+  auto split_of = [&](int i, int s) {
+    return pre[i] == 0 ? 1 : std::max(1, std::min(s, (pre[i] + kMinSplit - 1) / kMinSplit));
+  };
+  int best_s = 1;
+  double best_t = 0;
+  for (int s = 1; s <= kMaxSplits; ++s) {
+    double items = 0, work = 0, longest = 0, merge = 0;
+    for (int i = 0; i < n_req; ++i) {
+      if (n_q[i] == 0) continue;
+      const int si = split_of(i, s);
+      const int ti = (pre[i] + si * kKeys - 1) / (si * kKeys) + 1;  // tiles per item (+1 for the tail)
+      const double ni = static_cast<double>(tiles[i]) * Hkv * si;
+      items += ni;
+      work += ni * ti;
+      longest = std::max(longest, static_cast<double>(ti));
+      if (si > 1) merge += static_cast<double>(si) * n_q[i] * Hq;
+    }
+    if (items == 0) break;
+    const double t = std::max(longest, std::ceil(items / slots) * (work / items)) * tile_us + merge * row_us;
+    if (s == 1 || t < best_t * 0.98) {  // more splits only for a clear gain
+      best_s = s;
+      best_t = t;
+    }
+  }
   for (int i = 0; i < n_req; ++i) {
     if (pre[i] == 0) {
       splits[i] = 1;
       len[i] = 0;
       continue;
     }
-    long long s = std::min<long long>(std::min<long long>(factor, kMaxSplits), std::max(1, pre[i] / kMinSplit));
-    int l = static_cast<int>((pre[i] + s - 1) / s);
+    const int si = split_of(i, best_s);
+    int l = (pre[i] + si - 1) / si;
     l = (l + kKeys - 1) / kKeys * kKeys;
     len[i] = l;
     splits[i] = (pre[i] + l - 1) / l;
@@ -970,12 +1072,13 @@ void launch(const AttnPlan &P, bool paged, hipStream_t stream) {
 }  // namespace
 }  // namespace d3d
 
-extern "C" size_t draft_attn_packed_workspace(const int32_t *req_block_off, const int32_t *req_prefix_len,
-                                              int n_req, int block_size, int n_heads_q, int n_heads_kv,
-                                              int head_dim) {
+extern "C" size_t draft_attn_packed_workspace(d3d_dtype dtype, const int32_t *req_block_off,
+                                              const int32_t *req_prefix_len, int n_req, int block_size,
+                                              int n_heads_q, int n_heads_kv, int head_dim) {
+  if (dtype != D3D_BF16 && dtype != D3D_F32) return 0;
   d3d::AttnPlan P;
-  if (d3d::plan_attn(req_block_off, req_prefix_len, n_req, block_size, n_heads_q, n_heads_kv, head_dim, &P) !=
-      D3D_OK)
+  if (d3d::plan_attn(req_block_off, req_prefix_len, n_req, block_size, n_heads_q, n_heads_kv, head_dim,
+                     dtype == D3D_BF16 ? d3d::kBfRows : d3d::kRows, d3d::device_cus(), &P) != D3D_OK)
     return 0;
   return P.ws_bytes;
 }
@@ -990,7 +1093,8 @@ extern "C" int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_n
   using namespace d3d;
   if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
   AttnPlan P;
-  const int st = plan_attn(req_block_off, req_prefix_len, n_req, block_size, n_heads_q, n_heads_kv, head_dim, &P);
+  const int st = plan_attn(req_block_off, req_prefix_len, n_req, block_size, n_heads_q, n_heads_kv, head_dim,
+                           dtype == D3D_BF16 ? kBfRows : kRows, device_cus(), &P);
   if (st != D3D_OK) return st;
   if (!q || !k_new || !v_new || !descs || !out) return D3D_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return D3D_EINVAL;

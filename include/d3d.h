@@ -110,9 +110,12 @@ int d3d_build_branch_descs(int block_size, int coverage, int fanout, int prefix_
  * ------------------------------------------------------------------------------------------- */
 #define D3D_ATTN_MAX_REQ 64
 
-size_t draft_attn_packed_workspace(const int32_t *req_block_off, const int32_t *req_prefix_len,
-                                   int n_req, int block_size, int n_heads_q, int n_heads_kv,
-                                   int head_dim);
+/* Workspace bytes draft_attn_packed needs for this dtype, request layout and head shape on the
+ * current device (the number of key splits depends on the device's compute-unit count); 0 when no
+ * workspace is needed or the arguments are invalid. */
+size_t draft_attn_packed_workspace(d3d_dtype dtype, const int32_t *req_block_off,
+                                   const int32_t *req_prefix_len, int n_req, int block_size,
+                                   int n_heads_q, int n_heads_kv, int head_dim);
 
 int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_new, const void *v_new,
                       const void *k_cache, const void *v_cache, const int32_t *page_table,

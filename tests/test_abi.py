@@ -91,9 +91,18 @@ def test_host_validation_returns_before_launch():
 
 
 def test_workspace_sizes():
-    # async pack, 384 queries, 4096-token prefix: 8 splits of 512 keys
-    assert _binding.draft_attn_packed_workspace([0, 24], [4096], 16, 32, 8, 128) == 8 * 384 * 32 * 130 * 4
-    # a serving batch of 16 requests has enough groups that no request is split
-    assert _binding.draft_attn_packed_workspace(list(range(0, 17 * 24, 24)), [4096] * 16, 16, 32, 8, 128) == 0
+    # async pack, 384 queries, 4096-token prefix: too few (row tile, head) items for the device, so the
+    # prefix is cut into s key splits; the workspace holds s fp32 partial rows (d values + max + sum)
+    # per query-head row
+    per_split = 384 * 32 * 130 * 4
+    for dt in ("bf16", "f32"):
+        ws = _binding.draft_attn_packed_workspace(dt, [0, 24], [4096], 16, 32, 8, 128)
+        assert ws % per_split == 0 and 2 <= ws // per_split <= 16, (dt, ws)
+    # a serving batch of 16 requests has enough items that no request is split
+    assert _binding.draft_attn_packed_workspace("bf16", list(range(0, 17 * 24, 24)), [4096] * 16, 16, 32, 8, 128) == 0
+    # no prefix: nothing to split
+    assert _binding.draft_attn_packed_workspace("bf16", [0, 24], [0], 16, 32, 8, 128) == 0
+    # invalid head shape
+    assert _binding.draft_attn_packed_workspace("bf16", [0, 24], [4096], 16, 32, 8, 96) == 0
     assert _binding.spec_verify_workspace(16, 15, 151936) > 0
     assert _binding.spec_verify_workspace(1, 64, 10) == 0

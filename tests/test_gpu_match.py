@@ -100,7 +100,7 @@ def test_graph_replays_match_eager():
     tok = torch.from_numpy(vin["tokens"]).cuda()
     off_dev = torch.tensor(prob.off, dtype=torch.int32).cuda()
     out = torch.empty_like(prob.q)
-    need = _binding.draft_attn_packed_workspace(prob.off, prob.pre, B, 32, 8, 128)
+    need = _binding.draft_attn_packed_workspace("bf16", prob.off, prob.pre, B, 32, 8, 128)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     vws = torch.empty(_binding.spec_verify_workspace(1, B - 1, 4096), dtype=torch.uint8, device="cuda")
     res = dict(n_accepted=torch.empty(1, dtype=torch.int32, device="cuda"),
