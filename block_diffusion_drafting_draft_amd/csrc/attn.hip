@@ -445,6 +445,8 @@ __device__ __forceinline__ void tile1(const char *kst, const char *vst, const Fr
   using TT = DmaTile<D>;
   // The fragment reads are fenced into halves (scheduling barriers) so that at most half a tile of
   // K or V fragments is in flight: the other wavefront of the SIMD covers the LDS latency.
+  // Each k-step's two K fragments are read one step ahead of their MFMAs (scheduling groups: the
+  // reads of steps 0 and 1, then per step two MFMAs and the next step's reads).
   f32x16 s[2] = {};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -455,6 +457,13 @@ __device__ __forceinline__ void tile1(const char *kst, const char *vst, const Fr
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kst + fa.kof(kk) + 32 * mb * TT::RB);
         s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q[kk], s[mb], 0, 0, 0);
       }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);  // reads of the first two k-steps
+#pragma unroll
+    for (int kk = 0; kk < D / 32 - 2; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 2);  // MFMAs of step kk
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);  // reads of step kk + 2
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);  // MFMAs of the last two steps
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (MASK) {
@@ -465,12 +474,22 @@ __device__ __forceinline__ void tile1(const char *kst, const char *vst, const Fr
         s[mb][r] = visible(mb * 32 + 8 * (r >> 2) + (r & 3)) ? s[mb][r] : -INFINITY;
       }
   }
-  float mx = -INFINITY;
+  // row maximum: a max3 tree over the lane's 32 keys, then the other half of the column (lane ^ 32)
+  // through the half swap, which leaves the lane's own value in one result and its partner's in the
+  // other
+  float m1[11];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  for (int i = 0; i < 10; ++i) {
+    const int x = 3 * i, y = 3 * i + 1, z = 3 * i + 2;
+    m1[i] = fmaxf(fmaxf(s[x >> 4][x & 15], s[y >> 4][y & 15]), s[z >> 4][z & 15]);
+  }
+  m1[10] = fmaxf(s[1][14], s[1][15]);
+  float mx = fmaxf(fmaxf(fmaxf(fmaxf(m1[0], m1[1]), m1[2]), fmaxf(fmaxf(m1[3], m1[4]), m1[5])),
+                   fmaxf(fmaxf(fmaxf(m1[6], m1[7]), m1[8]), fmaxf(m1[9], m1[10])));
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
   const float mt = mx * c;
   const bool up = mt > st.m + kSlack;  // m = -inf: any finite maximum moves it
   if (__ballot(up)) {
@@ -487,6 +506,7 @@ __device__ __forceinline__ void tile1(const char *kst, const char *vst, const Fr
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   bf16x8 p[4];
+  float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains for the row sum
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -495,9 +515,11 @@ __device__ __forceinline__ void tile1(const char *kst, const char *vst, const Fr
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bf16x2 pr = {p[t][2 * u], p[t][2 * u + 1]};
-      st.l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, st.l, false);
+      part[u] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, part[u], false);
     }
   }
+  st.l += (part[0] + part[1]) + (part[2] + part[3]);
+  // V^T fragments likewise one MFMA ahead (two transposing reads each).
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     __builtin_amdgcn_sched_barrier(0);
@@ -511,6 +533,13 @@ __device__ __forceinline__ void tile1(const char *kst, const char *vst, const Fr
         st.o[b] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8 *>(both), p[t], st.o[b], 0, 0, 0);
       }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);  // fragments of the first two MFMAs
+#pragma unroll
+    for (int i = 0; i < D / 16 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 3);
   }
 }
 
