@@ -51,7 +51,8 @@ struct ReqInfo {
   int32_t q_begin;      // global packed row of the request's first query
   int32_t n_q;          // packed query rows of the request
   int32_t prefix;       // prefix length
-  int32_t split_len;    // keys per split (multiple of 64), 0 when the prefix is empty
+  int32_t split_len;    // keys per split after the first (multiple of 64), 0 when the prefix is empty
+  int32_t split0_len;   // keys of the first split, which also walks the in-pack tail
   int32_t n_splits;
   int32_t group_begin;  // first (split, kv head) group of the request in dispatch order
   int32_t block_begin;  // global index of the request's current block
@@ -121,8 +122,8 @@ __device__ __forceinline__ bool decode_item(const AttnArgs &a, Item &it) {
   it.split = gl / a.Hkv;
   it.g = gl - it.split * a.Hkv;
   if (it.tile >= (it.R.n_q + a.Qt - 1) / a.Qt) return false;
-  it.k0 = it.split * it.R.split_len;
-  it.k1 = min(it.R.prefix, it.k0 + it.R.split_len);
+  it.k0 = it.split == 0 ? 0 : it.R.split0_len + (it.split - 1) * it.R.split_len;
+  it.k1 = min(it.R.prefix, it.split == 0 ? it.R.split0_len : it.k0 + it.R.split_len);
   return true;
 }
 
@@ -988,7 +989,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   a.Qt = Qt;
   a.n_new = static_cast<int>(total_q);
 
-  std::vector<int> n_q(n_req), tiles(n_req), splits(n_req), len(n_req);
+  std::vector<int> n_q(n_req), tiles(n_req), splits(n_req), len(n_req), len0(n_req);
   for (int i = 0; i < n_req; ++i) {
     n_q[i] = (off[i + 1] - off[i]) * B;
     tiles[i] = (n_q[i] + Qt - 1) / Qt;
@@ -1019,17 +1020,33 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
       best_t = t;
     }
   }
+  // The first split also walks the in-pack tail (at most ceil((B + Qt) / 64) tiles), so it gets that
+  // many fewer prefix keys and every split carries about the same number of tiles.
+  const int tail_keys = (B + Qt + kKeys - 1) / kKeys * kKeys;
   for (int i = 0; i < n_req; ++i) {
     if (pre[i] == 0) {
       splits[i] = 1;
-      len[i] = 0;
+      len[i] = len0[i] = 0;
       continue;
     }
     const int si = split_of(i, best_s);
-    int l = (pre[i] + si - 1) / si;
-    l = (l + kKeys - 1) / kKeys * kKeys;
+    if (si == 1) {
+      splits[i] = 1;
+      len[i] = len0[i] = pre[i];
+      continue;
+    }
+    const int share = ((pre[i] + tail_keys + si - 1) / si + kKeys - 1) / kKeys * kKeys;
+    const int l0 = std::max(kKeys, std::min(pre[i], share - tail_keys));
+    const int rest = pre[i] - l0;
+    if (rest <= 0) {
+      splits[i] = 1;
+      len[i] = len0[i] = pre[i];
+      continue;
+    }
+    int l = ((rest + si - 2) / (si - 1) + kKeys - 1) / kKeys * kKeys;
+    len0[i] = l0;
     len[i] = l;
-    splits[i] = (pre[i] + l - 1) / l;
+    splits[i] = 1 + (rest + l - 1) / l;
   }
   // longest work item first (per-item keys; ties keep request order)
   std::vector<int> order;
@@ -1050,6 +1067,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
     R.n_q = n_q[i];
     R.prefix = pre[i];
     R.split_len = len[i];
+    R.split0_len = len0[i];
     R.n_splits = splits[i];
     R.group_begin = groups;
     R.block_begin = off[i];
