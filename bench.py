@@ -9,7 +9,8 @@ A step is one pass of the whole hot path over one synthetic round of the async w
   3. spec_verify (stats, decide, residual / bonus sample),
   4. branch_cache_match.
 Inputs are resident in HBM before the timed region. The device part of a step (2-4) is captured
-once in a HIP graph; each step builds its descriptors on the host into a ring of pinned buffers,
+once in a HIP graph, with 2 and 3 on two streams (they are independent within a round: drafting the
+next block's branches overlaps verifying the current block) joined before 4; each step builds its descriptors on the host into a ring of pinned buffers,
 enqueues their copy and replays the graph. W untimed warm-up steps, then K timed steps between
 device synchronisations. Per-call durations come from HIP events recorded on the launch stream
 around K replays of a graph holding only that call. Prints one JSON line.
@@ -71,6 +72,7 @@ class Round:
         cu = lambda x: bits(x).cuda()
         self.B = w.block_size
         self.lens = self.ain["prefix"]
+        self.lens_i32 = np.asarray(self.lens, dtype=np.int32)
         self.n_req = len(self.lens)
         self.q, self.k_new, self.v_new = cu(self.ain["q"]), cu(self.ain["k_new"]), cu(self.ain["v_new"])
         if w.paged:
@@ -96,6 +98,9 @@ class Round:
         self.desc_host = torch.empty((n_blk, 4), dtype=torch.int32, pin_memory=True)
         self.descs = torch.empty((n_blk, 4), dtype=torch.int32, device="cuda")
         self.off_dev = torch.from_numpy(self.off).cuda()
+        self.off_scratch = np.zeros(self.n_req + 1, dtype=np.int32)
+        self.cur_anchor = np.ascontiguousarray(self.vin["cur_anchor"], dtype=np.int32)
+        self.alt_anchors = np.ascontiguousarray(self.vin["alt_anchors"], dtype=np.int32) if w.coverage else None
         self.out = torch.empty_like(self.q)
         need = _binding.draft_attn_packed_workspace(self.q.dtype, self.off, self.lens, self.B, self.q.shape[1],
                                                     self.k_new.shape[1], self.q.shape[2])
@@ -115,19 +120,17 @@ class Round:
     def build_descs(self, pinned=None):
         w = self.w
         host = (self.desc_host if pinned is None else pinned).numpy()
-        for i in range(self.n_req):
-            a, b = self.off[i], self.off[i + 1]
-            if w.coverage:
-                host[a:b] = self.lib.d3d_build_branch_descs(self.B, w.coverage, w.fanout, self.lens[i],
-                                                            int(self.vin["cur_anchor"][i]), self.vin["alt_anchors"][i])
-            else:
-                host[a:b] = (self.lens[i], 0, int(self.vin["cur_anchor"][i]), 0)
+        if w.coverage:
+            self.lib.d3d_build_branch_descs_batch(self.B, w.coverage, w.fanout, self.lens_i32, self.cur_anchor,
+                                                  self.alt_anchors, out=host, req_block_off=self.off_scratch)
+        else:
+            host[:, 0], host[:, 1], host[:, 2], host[:, 3] = self.lens, 0, self.cur_anchor, 0
         if pinned is None:
             self.descs.copy_(self.desc_host, non_blocking=True)
 
     def attention(self):
         self.lib.draft_attn_packed(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.descs,
-                                   self.off, self.lens, self.B, page_table=self.page_table,
+                                   self.off, self.lens_i32, self.B, page_table=self.page_table,
                                    page_size=self.w.page_size, out=self.out, ws=self.attn_ws)
 
     def verify(self):
@@ -217,9 +220,18 @@ def main():
     ring = [torch.empty_like(r.desc_host).pin_memory() for _ in range(3)]
     copied = [torch.cuda.Event() for _ in ring]
 
+    side = torch.cuda.Stream()  # default priority
+
     def device_round():
+        # The drafter's packed attention (branches for the next block) and the target's verify of the
+        # current block are independent within a round: they run on two streams, and the cache match,
+        # which needs the verify outcome and the branch descriptors, joins them.
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            r.verify()
         r.attention()
-        r.verify()
+        cur.wait_stream(side)
         r.match()
 
     for _ in range(3):  # eager warm-up (first launches, code-object loads)

@@ -5,7 +5,7 @@ exported here are its thin Python binding with the same names. Build the library
 ``python -m block_diffusion_drafting_draft_amd.build``.
 """
 
-_BOUND = ("d3d_build_branch_descs", "draft_attn_packed_workspace", "draft_attn_packed",
+_BOUND = ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "draft_attn_packed_workspace", "draft_attn_packed",
           "spec_verify_workspace", "spec_verify", "branch_cache_match")
 
 __all__ = list(_BOUND)

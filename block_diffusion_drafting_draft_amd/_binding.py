@@ -20,11 +20,13 @@ BLOCK_CAUSAL = 1
 MAX_REQ = 64
 
 _c = ctypes
-_i32p = _c.POINTER(_c.c_int32)
+_i32p = _c.c_void_p  # host int32 array, passed as its address
 
 _SIGNATURES = {
     "d3d_build_branch_descs": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int32, _i32p,
                                            _c.c_void_p, _c.c_int, _c.POINTER(_c.c_int)]),
+    "d3d_build_branch_descs_batch": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _i32p, _i32p, _i32p,
+                                                 _c.c_void_p, _c.c_int, _i32p]),
     "draft_attn_packed_workspace": (_c.c_size_t, [_c.c_int, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int,
                                                   _c.c_int, _c.c_int]),
     "draft_attn_packed": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
@@ -69,11 +71,11 @@ def _check(status, what):
 
 def _host_i32(x):
     a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
-    return a, a.ctypes.data_as(_i32p)
+    return a, a.ctypes.data
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream(stream):
@@ -109,9 +111,36 @@ def d3d_build_branch_descs(block_size, coverage, fanout, prefix_len, cur_anchor,
     out = np.zeros((max(cap, 1), 4), dtype=np.int32)
     n = ctypes.c_int(0)
     _check(load().d3d_build_branch_descs(block_size, coverage, fanout, prefix_len, int(cur_anchor), alt_p,
-                                         out.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n)),
+                                         out.ctypes.data, cap, ctypes.byref(n)),
            "d3d_build_branch_descs")
     return out[:n.value]
+
+
+def d3d_build_branch_descs_batch(block_size, coverage, fanout, prefix_len, cur_anchor, alt_anchors, out=None,
+                                 req_block_off=None):
+    """Batched host descriptor builder. prefix_len / cur_anchor: [n_req]; alt_anchors: [n_req, (C-1)F + 1].
+    out: optional int32 array [>= n_req ((C-1)F + 2), 4] (a numpy view of pinned memory works);
+    req_block_off: optional int32 array [n_req + 1]. Returns (descs, req_block_off) as numpy arrays."""
+    pre, pre_p = _host_i32(prefix_len)
+    cur, cur_p = _host_i32(cur_anchor)
+    alt, alt_p = _host_i32(alt_anchors)
+    n_req = pre.size
+    per = (coverage - 1) * fanout + 2
+    if cur.size != n_req or alt.size != n_req * (per - 1):
+        raise ValueError("cur_anchor / alt_anchors do not match prefix_len")
+    if out is None:
+        out = np.zeros((max(n_req * per, 1), 4), dtype=np.int32)
+    if out.dtype != np.int32 or not out.flags.c_contiguous or out.ndim != 2 or out.shape[1] != 4:
+        raise ValueError("out must be a C-contiguous int32 array [cap, 4]")
+    if req_block_off is None:
+        req_block_off = np.zeros(n_req + 1, dtype=np.int32)
+    if req_block_off.dtype != np.int32 or not req_block_off.flags.c_contiguous or req_block_off.size < n_req + 1:
+        raise ValueError("req_block_off must be a C-contiguous int32 array of n_req + 1 entries")
+    _check(load().d3d_build_branch_descs_batch(n_req, block_size, coverage, fanout, pre_p, cur_p, alt_p,
+                                               out.ctypes.data, out.shape[0],
+                                               req_block_off.ctypes.data),
+           "d3d_build_branch_descs_batch")
+    return out[:n_req * per], req_block_off[:n_req + 1]
 
 
 def draft_attn_packed_workspace(dtype, req_block_off, req_prefix_len, block_size, n_heads_q, n_heads_kv,

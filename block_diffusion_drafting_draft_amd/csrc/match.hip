@@ -74,6 +74,29 @@ extern "C" int d3d_build_branch_descs(int block_size, int coverage, int fanout, 
   return D3D_OK;
 }
 
+extern "C" int d3d_build_branch_descs_batch(int n_req, int block_size, int coverage, int fanout,
+                                            const int32_t *prefix_len, const int32_t *cur_anchor,
+                                            const int32_t *alt_anchors, d3d_block_desc *out, int cap,
+                                            int32_t *req_block_off) {
+  if (n_req < 1 || !prefix_len || !cur_anchor || !alt_anchors || !out || !req_block_off) return D3D_EINVAL;
+  if (block_size < 1 || block_size > 64 || coverage < 2 || coverage > block_size || fanout < 1) return D3D_EINVAL;
+  const long long per = static_cast<long long>(coverage - 1) * fanout + 2;
+  if (per * n_req > cap) return D3D_EINVAL;
+  for (int i = 0; i < n_req; ++i)
+    if (prefix_len[i] < 0) return D3D_EINVAL;
+  const int na = static_cast<int>(per - 1);  // anchors per request
+  req_block_off[0] = 0;
+  for (int i = 0; i < n_req; ++i) {
+    int n = 0;
+    const int st = d3d_build_branch_descs(block_size, coverage, fanout, prefix_len[i], cur_anchor[i],
+                                          alt_anchors + static_cast<size_t>(i) * na, out + per * i,
+                                          static_cast<int>(per), &n);
+    if (st != D3D_OK) return st;
+    req_block_off[i + 1] = req_block_off[i] + n;
+  }
+  return D3D_OK;
+}
+
 extern "C" const char *d3d_status_string(int status) {
   switch (status) {
     case D3D_OK: return "ok";

@@ -75,6 +75,17 @@ int d3d_build_branch_descs(int block_size, int coverage, int fanout, int prefix_
                            int32_t cur_anchor, const int32_t *alt_anchors,
                            d3d_block_desc *out, int cap, int *n_out);
 
+/* The same for a batch of n_req requests with a common (B, C, F), as a serving scheduler builds
+ * them each round: request i's (C-1)F + 2 descriptors are written at out[i * ((C-1)F + 2)], in the
+ * order above, from prefix_len[i], cur_anchor[i] and the (C-1)F + 1 anchors at
+ * alt_anchors[i * ((C-1)F + 1)] (all host arrays). req_block_off (host, n_req + 1 entries) receives
+ * the packed block offsets draft_attn_packed takes.
+ * Errors: D3D_EINVAL on a bad argument or cap < n_req ((C-1)F + 2) (out may be partly written). */
+int d3d_build_branch_descs_batch(int n_req, int block_size, int coverage, int fanout,
+                                 const int32_t *prefix_len, const int32_t *cur_anchor,
+                                 const int32_t *alt_anchors, d3d_block_desc *out, int cap,
+                                 int32_t *req_block_off);
+
 /* ---------------------------------------------------------------------------------------------
  * Packed draft attention -- one drafter attention layer of the packed forward ([D3D] 核心方法:
  * prefix shared and causally encoded, attention bidirectional inside a block; 方法步骤详情 step 4).

@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for want in ("d3d_build_branch_descs", "draft_attn_packed", "draft_attn_packed_workspace",
+    for want in ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "draft_attn_packed", "draft_attn_packed_workspace",
                  "spec_verify", "spec_verify_workspace", "branch_cache_match", "d3d_status_string"):
         assert want in names
 
@@ -45,6 +45,25 @@ def test_descriptor_builder_matches_oracle_packing(B, C, F, L):
     assert len(blocks) * B == packing.n_async(B, C, F)
     for row, (r, anchor, causal) in zip(d, blocks):
         assert tuple(int(x) for x in row) == (L, r, anchor, 1 if causal else 0)
+
+
+@pytest.mark.parametrize("B,C,F", [(16, 12, 2), (32, 16, 5), (4, 3, 1)])
+def test_batched_descriptor_builder_matches_per_request(B, C, F):
+    rng = np.random.default_rng(7 * B + C)
+    n_req = 5
+    lens = rng.integers(0, 9000, size=n_req)
+    cur = rng.integers(0, 151936, size=n_req)
+    alt = rng.integers(0, 151936, size=(n_req, (C - 1) * F + 1))
+    out = np.full((n_req * ((C - 1) * F + 2) + 3, 4), -7, dtype=np.int32)
+    d, off = _binding.d3d_build_branch_descs_batch(B, C, F, lens, cur, alt, out=out)
+    want = [_binding.d3d_build_branch_descs(B, C, F, int(lens[i]), int(cur[i]), alt[i]) for i in range(n_req)]
+    assert np.array_equal(d, np.concatenate(want))
+    assert off.tolist() == np.concatenate([[0], np.cumsum([len(w) for w in want])]).tolist()
+    assert (out[len(d):] == -7).all()  # nothing written past the batch
+    with pytest.raises(RuntimeError, match="status -1"):
+        _binding.d3d_build_branch_descs_batch(B, C, F, lens, cur, alt, out=out[:len(d) - 1])
+    with pytest.raises(RuntimeError, match="status -1"):
+        _binding.d3d_build_branch_descs_batch(B, C, F, np.r_[lens[:-1], -1], cur, alt)
 
 
 def test_descriptor_builder_rejects_bad_arguments():
