@@ -5,22 +5,29 @@
 // draft, the first rejection against Philox uniforms, the residual max(0, P - Q) or bonus draw,
 // the prefix-survival products S(k) and tau = 1 + sum_k S(k).
 //
-// Design (HBM-bound: the whole vocabulary of every row is read once):
-//   1. stats   grid (chunk, row): one coalesced 16-byte-vector pass over a slice of one logit row:
-//              running max (and first argmax), sum of exp((z - max)/T) with fp32 exp2 per element
-//              and fp64 accumulation per thread. Partial (max, argmax, sum) per (row, chunk).
-//   2. decide  one wavefront per request: merges the row partials in fp64, forms alpha_j from
-//              fp64 scalars, draws the Philox uniforms, finds the first rejection, S(k), tau.
-//   3. lse     grid (chunk, request): fp64 sum of exp((z - max)/T) over the one or two rows the
-//              draw needs (target row j*, and draft row j* after a rejection).
-//   4. mass    grid (chunk, request): fp64 residual (or bonus) mass per chunk.
-//   5. pick    one workgroup per request: chunk-level prefix over the masses, then a workgroup
-//              scan inside the chunk that holds u'Z, returning the smallest token whose inclusive
+// Design (HBM-bound: the whole vocabulary of every row is read once; everything after that pass
+// touches one or two rows per request and is latency-bound, so it is built from few dependent
+// memory round trips):
+//   1. stats   grid (chunk, row), one round of resident workgroups: one coalesced 16-byte-vector
+//              pass over a slice of one logit row: running max (and first argmax), sum of
+//              exp((z - max)/T) with fp32 exp2 per element and fp64 accumulation per thread, and
+//              the logit at the row's draft token when the slice holds it. Partial per (row, chunk).
+//   2. decide + lse   grid (sample chunk, request): every workgroup stages its request's partials
+//              in LDS, merges each row in fp64, forms alpha_j from fp64 scalars, draws the Philox
+//              uniforms, finds the first rejection, S(k) and tau (the chunk-0 workgroup stores
+//              them); then the fp64 sum of exp((z - max)/T) over its 2048-token slice of the one or
+//              two rows the draw needs (target row j*, and draft row j* after a rejection).
+//   3. mass    grid (sample chunk, request): fp64 residual (or bonus) mass of each slice.
+//   4. pick    one workgroup per request: prefix over the slice masses, then a workgroup scan
+//              inside the slice that holds u'Z, returning the smallest token whose inclusive
 //              cumulative mass exceeds u'Z.
+// The sample passes read 8 consecutive tokens per thread with one 16-byte load per row.
 // Nothing returns to the host; every pass is stream-ordered after the previous one.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
+
+#include <algorithm>
 
 #include "d3d_internal.h"
 
@@ -29,17 +36,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kStatTargetBlocks = 2048;
+constexpr int kStatSlots = 2048;  // stats workgroups resident at once: 8 per CU on 256 CUs
 constexpr int kStatMinChunk = 1024;
-constexpr int kSampleTargetBlocks = 2048;
-constexpr int kSampleMinChunk = 256;
+constexpr int kSampleElems = 8;                        // tokens per thread in the sample passes
+constexpr int kSampleChunk = kThreads * kSampleElems;  // tokens per sample workgroup
 constexpr int kMaxSampleChunks = 1024;
+constexpr int kMaxReqPartials = 2048;  // stats partials of one request staged in LDS by decide
 constexpr double kNear = 1e-6;
 
 struct StatPartial {
   float max;
-  int32_t arg;
-  double sum;  // sum of exp((z - max) / T) over the chunk
+  int32_t aux;  // greedy: first argmax; sampling: bits of the logit at the row's draft token when
+                // this chunk holds that token, else 0
+  double sum;   // sum of exp((z - max) / T) over the chunk
 };
 
 enum SampleMode : int32_t { kDone = 0, kResidual = 1, kBonus = 2 };
@@ -60,7 +69,7 @@ struct VerifyArgs {
   const int32_t *tokens;
   int n_req, n_draft, vocab, n_tgt_rows;
   int chunks, chunk_len;
-  int s_chunks, s_chunk_len;
+  int s_chunks;
   float c_log2;    // log2(e) / T
   double inv_t;    // 1 / T (fp64)
   uint64_t seed;
@@ -77,6 +86,36 @@ struct VerifyArgs {
   double *lse_part;   // [n_req][s_chunks][2]
   double *mass_part;  // [n_req][s_chunks]
 };
+
+// exp(x) in fp64 for x <= 0, the only arguments produced here (differences from a running or row
+// maximum, or log-probabilities). Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software
+// Manual for the Elementary Functions", 1980): x = k ln2 + r with |r| <= ln2/2, ln2 split into a
+// 21-bit head (k * head is exact) and a tail; then the Taylor series of e^r to degree 12
+// (truncation below 2e-16 relative) and a scaling by 2^k. About 18 fp64 operations. NaN (from
+// -inf - -inf) and arguments below the smallest subnormal give 0.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  constexpr double kInvLn2 = 1.4426950408889634;
+  constexpr double kLn2Hi = 0.6931467056274414;      // ln 2 with its low 32 mantissa bits cleared
+  constexpr double kLn2Lo = 4.7493250390316726e-07;  // ln 2 - kLn2Hi
+  if (!(x > -745.5)) return 0.0;
+  const double k = rint(x * kInvLn2);
+  double r = fma(-k, kLn2Hi, x);
+  r = fma(-k, kLn2Lo, r);
+  double p = 2.08767569878681e-09;  // 1/12!
+  p = fma(p, r, 2.505210838544172e-08);
+  p = fma(p, r, 2.755731922398589e-07);
+  p = fma(p, r, 2.7557319223985893e-06);
+  p = fma(p, r, 2.48015873015873e-05);
+  p = fma(p, r, 0.0001984126984126984);
+  p = fma(p, r, 0.001388888888888889);
+  p = fma(p, r, 0.008333333333333333);
+  p = fma(p, r, 0.041666666666666664);
+  p = fma(p, r, 0.16666666666666666);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, static_cast<int>(k));
+}
 
 // ------------------------------------------------------------------------------------------------
 // block reductions (256 threads = 4 wavefronts)
@@ -123,7 +162,7 @@ struct RowAcc {
   double s = 0.0;
   int arg = INT_MAX;
 
-  // Fold 8 consecutive elements starting at token index `idx` (z in fp32, exact for bf16).
+  // Fold N consecutive elements starting at token index `idx` (z in fp32, exact for bf16).
   template <int N>
   __device__ __forceinline__ void fold(const float (&z)[N], int idx, float c_log2, double inv_t) {
     float vm = z[0];
@@ -140,9 +179,10 @@ struct RowAcc {
       }
     } else {
       if (vm > m) {
-        if (m != -INFINITY) s *= exp(static_cast<double>(m - vm) * inv_t);
+        if (m != -INFINITY) s *= exp_nonpos((static_cast<double>(m) - vm) * inv_t);
         m = vm;
       }
+      if (m == -INFINITY) return;  // every logit so far is -inf: no mass yet
       float part = 0.f;
 #pragma unroll
       for (int k = 0; k < N; ++k) part += __builtin_amdgcn_exp2f((z[k] - m) * c_log2);
@@ -163,6 +203,21 @@ __device__ __forceinline__ void unpack(const u32x4 &w, float (&z)[4], const floa
   for (int k = 0; k < 4; ++k) z[k] = __uint_as_float(w[k]);
 }
 
+// The draft token a row judges (target row j < n_draft or draft row j), or -1 for the bonus row.
+__device__ __forceinline__ int row_token(const VerifyArgs &a, int row) {
+  int i, j;
+  if (row < a.n_tgt_rows) {
+    i = row / (a.n_draft + 1);
+    j = row - i * (a.n_draft + 1);
+    if (j == a.n_draft) return -1;
+  } else {
+    const int r = row - a.n_tgt_rows;
+    i = r / a.n_draft;
+    j = r - i * a.n_draft;
+  }
+  return min(max(a.tokens[static_cast<size_t>(i) * a.n_draft + j], 0), a.vocab - 1);
+}
+
 template <typename T, bool VEC, bool GREEDY>
 __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
   __shared__ float sh_f[kWaves];
@@ -176,6 +231,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
                             static_cast<size_t>(row - a.n_tgt_rows) * a.vocab;
   const int begin = chunk * a.chunk_len;
   const int end = min(begin + a.chunk_len, a.vocab);
+  // the logit at the row's draft token, read up front (a wave-uniform load) when this chunk holds it
+  const int y = GREEDY ? -1 : row_token(a, row);
+  const bool has_y = y >= begin && y < end;
+  float zy = 0.f;
+  if (has_y) zy = load_elem(base + y);
   RowAcc<GREEDY> acc;
   if constexpr (VEC) {
     constexpr int W = 16 / sizeof(T);
@@ -209,95 +269,109 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
   StatPartial out;
   out.max = m;
   if constexpr (GREEDY) {
-    out.arg = block_min_int(acc.m == m ? acc.arg : INT_MAX, sh_i);
+    out.aux = block_min_int(acc.m == m ? acc.arg : INT_MAX, sh_i);
     out.sum = 0.0;
   } else {
-    const double mine = acc.m == -INFINITY ? 0.0 : acc.s * exp(static_cast<double>(acc.m - m) * a.inv_t);
+    const double mine =
+        acc.m == -INFINITY ? 0.0 : acc.s * exp_nonpos((static_cast<double>(acc.m) - m) * a.inv_t);
     out.sum = block_sum(mine, sh_d);
-    out.arg = 0;
+    out.aux = has_y ? __float_as_int(zy) : 0;
   }
   if (threadIdx.x == 0) a.stats[static_cast<size_t>(row) * a.chunks + chunk] = out;
 }
 
 // ------------------------------------------------------------------------------------------------
-// 2. decide
+// 2. decide (run by every workgroup of the lse pass for its request)
 // ------------------------------------------------------------------------------------------------
-// Merge one row's chunk partials with one wavefront (lanes stride over chunks): exact max, first
-// argmax, and the fp64 sum of exp((z - max)/T) rescaled from each chunk's own max.
-struct RowStat {
-  float max;
-  double sum;
-  int arg;
+// Local rows 0..nd are the request's target rows, nd+1..2nd its draft rows (greedy: target only).
+struct ReqRows {
+  float max[127];
+  double sum[127];
+  int arg[127];
+  float zy[127];  // logit at the row's draft token (rows with one)
+  int tok[63];
 };
 
-__device__ RowStat merge_row_wave(const VerifyArgs &a, int row) {
-  const int lane = threadIdx.x & 63;
-  const StatPartial *p = a.stats + static_cast<size_t>(row) * a.chunks;
-  float m = -INFINITY;
-  int arg = INT_MAX;
-  double s = 0.0;
-  for (int c = lane; c < a.chunks; c += 64) {
-    const StatPartial q = p[c];
-    if (q.max > m) {  // chunks are visited in increasing order: keep the first maximum
-      if (!a.greedy && m != -INFINITY) s *= exp(static_cast<double>(m - q.max) * a.inv_t);
-      m = q.max;
-      arg = q.arg;
-    }
-    if (!a.greedy) s += q.sum * exp(static_cast<double>(q.max - m) * a.inv_t);
-  }
-  float wm = m;
-  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
-  int warg = m == wm ? arg : INT_MAX;
-  for (int o = 32; o > 0; o >>= 1) warg = min(warg, __shfl_xor(warg, o));
-  double ws = 0.0;
-  if (!a.greedy) {
-    ws = m == -INFINITY ? 0.0 : s * exp(static_cast<double>(m - wm) * a.inv_t);
-    for (int o = 32; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
-  }
-  RowStat r;
-  r.max = wm;
-  r.sum = ws;
-  r.arg = warg;
-  return r;
-}
-
-// One workgroup per request. Local rows 0..nd are the target rows, nd+1..2nd the draft rows.
-constexpr int kDecideThreads = 1024;
-
-template <typename T>
-__global__ __launch_bounds__(kDecideThreads) void decide_kernel(const VerifyArgs a) {
-  __shared__ float sh_max[128];
-  __shared__ double sh_sum[128];
-  __shared__ int sh_arg[128];
-  const int i = blockIdx.x;
+// Loads the request's stats partials into LDS (one round trip), merges every row with a group of
+// g lanes (g a power of two, so a group never straddles a wavefront; lanes stride over chunks in
+// increasing order, which keeps the first argmax), then wavefront 0 takes the decisions. The
+// results are identical in every workgroup of the request; only `store` writes them out.
+__device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatPartial *part, ReqRows &rr,
+                               SampleState *sh_state, bool store) {
   const int nd = a.n_draft;
-  const int V = a.vocab;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int C = a.chunks;
   const int n_rows = a.greedy ? nd + 1 : 2 * nd + 1;
-  for (int r = wave; r < n_rows; r += kDecideThreads / 64) {
-    const int row = r <= nd ? i * (nd + 1) + r : a.n_tgt_rows + i * nd + (r - nd - 1);
-    const RowStat st = merge_row_wave(a, row);
-    if (lane == 0) {
-      sh_max[r] = st.max;
-      sh_sum[r] = st.sum;
-      sh_arg[r] = st.arg;
+  const int n_tp = (nd + 1) * C;
+  const int n_all = n_rows * C;
+  const StatPartial *tgt = a.stats + static_cast<size_t>(i) * n_tp;
+  const StatPartial *drf = a.stats + static_cast<size_t>(a.n_tgt_rows) * C + static_cast<size_t>(i) * nd * C;
+  {
+    // every load is issued (indexes clamped) before any LDS store, so this is one round trip
+    constexpr int K = kMaxReqPartials / kThreads;
+    static_assert(sizeof(StatPartial) == sizeof(u32x4), "a partial moves as one 16-byte vector");
+    u32x4 tmp[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int t = min(static_cast<int>(threadIdx.x) + k * kThreads, n_all - 1);
+      const StatPartial *src = t < n_tp ? tgt + t : drf + (t - n_tp);
+      tmp[k] = *reinterpret_cast<const u32x4 *>(src);
+    }
+    if (threadIdx.x < nd)
+      rr.tok[threadIdx.x] = min(max(a.tokens[static_cast<size_t>(i) * nd + threadIdx.x], 0), a.vocab - 1);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(part);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int t = static_cast<int>(threadIdx.x) + k * kThreads;
+      if (t < n_all) dst[t] = tmp[k];
     }
   }
   __syncthreads();
-  if (wave != 0) return;
+  int g = 64;
+  while (g > 1 && n_rows * g > kThreads) g >>= 1;
+  const int r = threadIdx.x / g, sub = threadIdx.x % g;
+  float m = -INFINITY;
+  int arg = INT_MAX;
+  double s = 0.0;
+  if (r < n_rows) {
+    for (int c = sub; c < C; c += g) {
+      const StatPartial q = part[r * C + c];
+      if (q.max > m) {
+        if (!a.greedy && m != -INFINITY) s *= exp_nonpos((static_cast<double>(m) - q.max) * a.inv_t);
+        m = q.max;
+        arg = q.aux;
+      }
+      if (!a.greedy && q.max != -INFINITY) s += q.sum * exp_nonpos((static_cast<double>(q.max) - m) * a.inv_t);
+    }
+  }
+  float wm = m;
+  for (int o = g >> 1; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
+  int warg = m == wm ? arg : INT_MAX;
+  for (int o = g >> 1; o > 0; o >>= 1) warg = min(warg, __shfl_xor(warg, o));
+  double ws = m == -INFINITY ? 0.0 : s * exp_nonpos((static_cast<double>(m) - wm) * a.inv_t);
+  for (int o = g >> 1; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+  if (sub == 0 && r < n_rows) {
+    rr.max[r] = wm;
+    rr.sum[r] = ws;
+    rr.arg[r] = warg;
+    const int j = r <= nd ? r : r - nd - 1;
+    if (!a.greedy && j < nd) {
+      const int y = rr.tok[j];
+      rr.zy[r] = __int_as_float(part[r * C + y / a.chunk_len].aux);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
   // lane j judges draft j
+  const int lane = threadIdx.x;
   const int j = lane;
   double alpha = 1.0, u = 1.0;
   if (j < nd) {
-    const int y = min(max(a.tokens[static_cast<size_t>(i) * nd + j], 0), V - 1);
     if (a.greedy) {
-      alpha = (y == sh_arg[j]) ? 1.0 : 0.0;
+      alpha = (rr.tok[j] == rr.arg[j]) ? 1.0 : 0.0;
     } else {
-      const T *zp = static_cast<const T *>(a.target) + (static_cast<size_t>(i) * (nd + 1) + j) * V;
-      const T *zq = static_cast<const T *>(a.draft) + (static_cast<size_t>(i) * nd + j) * V;
-      const double lp = (static_cast<double>(load_elem(zp + y)) - sh_max[j]) * a.inv_t - log(sh_sum[j]);
-      const double lq = (static_cast<double>(load_elem(zq + y)) - sh_max[nd + 1 + j]) * a.inv_t -
-                        log(sh_sum[nd + 1 + j]);
+      const double lp = (static_cast<double>(rr.zy[j]) - rr.max[j]) * a.inv_t - log(rr.sum[j]);
+      const double lq = (static_cast<double>(rr.zy[nd + 1 + j]) - rr.max[nd + 1 + j]) * a.inv_t -
+                        log(rr.sum[nd + 1 + j]);
       const double py = exp(lp), qy = exp(lq);
       alpha = qy > 0.0 ? fmin(1.0, py / qy) : 1.0;
     }
@@ -315,66 +389,50 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(const VerifyArgs
   }
   double tsum = j < nd ? surv : 0.0;
   for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o);
-  if (j < nd) {
+  if (store && j < nd) {
     if (a.alpha) a.alpha[static_cast<size_t>(i) * nd + j] = static_cast<float>(alpha);
     if (a.survival) a.survival[static_cast<size_t>(i) * nd + j] = static_cast<float>(surv);
   }
   if (lane == 0) {
-    a.n_acc[i] = n_acc;
-    if (a.tau) a.tau[i] = static_cast<float>(1.0 + tsum);
-    if (a.flags) a.flags[i] = near ? 1u : 0u;
     SampleState st;
     st.pad = 0;
     st.tgt_row = i * (nd + 1) + n_acc;
     st.drf_row = i * nd + min(n_acc, nd - 1);  // never read in bonus mode
-    st.max_p = sh_max[n_acc];
-    st.max_q = (!a.greedy && n_acc < nd) ? sh_max[nd + 1 + n_acc] : 0.f;
+    st.max_p = rr.max[n_acc];
+    st.max_q = (!a.greedy && n_acc < nd) ? rr.max[nd + 1 + n_acc] : 0.f;
     st.u = philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
-    if (a.greedy) {
-      st.mode = kDone;
-      a.next_token[i] = sh_arg[n_acc];
-    } else {
-      st.mode = n_acc < nd ? kResidual : kBonus;
+    st.mode = a.greedy ? kDone : (n_acc < nd ? kResidual : kBonus);
+    *sh_state = st;
+    if (store) {
+      a.n_acc[i] = n_acc;
+      if (a.tau) a.tau[i] = static_cast<float>(1.0 + tsum);
+      if (a.flags) a.flags[i] = near ? 1u : 0u;
+      if (a.greedy) a.next_token[i] = rr.arg[n_acc];
+      else a.state[i] = st;
     }
-    a.state[i] = st;
   }
 }
 
-// exp(x) in fp64 for x <= 0, the only arguments the sample passes produce (logits minus their row
-// max, or log-probabilities). Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software Manual
-// for the Elementary Functions", 1980): x = k ln2 + r with |r| <= ln2/2, ln2 split into a 21-bit
-// head (k * head is exact) and a tail; then the Taylor series of e^r to degree 12 (truncation below
-// 2e-16 relative) and a scaling by 2^k. About 18 fp64 operations.
-__device__ __forceinline__ double exp_nonpos(double x) {
-  constexpr double kInvLn2 = 1.4426950408889634;
-  constexpr double kLn2Hi = 0.6931467056274414;      // ln 2 with its low 32 mantissa bits cleared
-  constexpr double kLn2Lo = 4.7493250390316726e-07;  // ln 2 - kLn2Hi
-  if (!(x > -745.5)) return 0.0;
-  const double k = rint(x * kInvLn2);
-  double r = fma(-k, kLn2Hi, x);
-  r = fma(-k, kLn2Lo, r);
-  double p = 2.08767569878681e-09;  // 1/12!
-  p = fma(p, r, 2.505210838544172e-08);
-  p = fma(p, r, 2.755731922398589e-07);
-  p = fma(p, r, 2.7557319223985893e-06);
-  p = fma(p, r, 2.48015873015873e-05);
-  p = fma(p, r, 0.0001984126984126984);
-  p = fma(p, r, 0.001388888888888889);
-  p = fma(p, r, 0.008333333333333333);
-  p = fma(p, r, 0.041666666666666664);
-  p = fma(p, r, 0.16666666666666666);
-  p = fma(p, r, 0.5);
-  p = fma(p, r, 1.0);
-  p = fma(p, r, 1.0);
-  return ldexp(p, static_cast<int>(k));
-}
-
 // ------------------------------------------------------------------------------------------------
-// 3.-5. fp64 sample of the one row the next token is drawn from
+// 2.-4. fp64 sample of the one row the next token is drawn from
 // ------------------------------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ double centered(const T *row, int v, float mx, double inv_t) {
-  return (static_cast<double>(load_elem(row + v)) - static_cast<double>(mx)) * inv_t;
+// Eight consecutive logits from token v0 on; tokens past the vocabulary read as -inf (zero mass).
+template <typename T, bool VEC>
+__device__ __forceinline__ void load8(const T *row, int v0, int V, float (&z)[kSampleElems]) {
+  if (VEC && v0 + kSampleElems <= V) {
+    constexpr int W = 16 / sizeof(T);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(row + v0);
+#pragma unroll
+    for (int h = 0; h < kSampleElems / W; ++h) {
+      float t[W];
+      unpack(vp[h], t, static_cast<const T *>(nullptr));
+#pragma unroll
+      for (int k = 0; k < W; ++k) z[h * W + k] = t[k];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kSampleElems; ++k) z[k] = v0 + k < V ? load_elem(row + v0 + k) : -INFINITY;
+  }
 }
 
 template <typename T>
@@ -384,32 +442,63 @@ struct DrawRows {
   float mp, mq;
   double inv_t, log_sp, log_sq;
   int mode;
-  // Mass of token v in the law being drawn from: max(0, P - Q) after a rejection, P for the bonus
-  // draw or the zero-mass fallback (mode != kResidual).
-  __device__ __forceinline__ double mass(int v) const {
-    const double ap = centered(p, v, mp, inv_t) - log_sp;
+  // Mass of a token with target logit zp and draft logit zq in the law being drawn from:
+  // max(0, P - Q) after a rejection, P for the bonus draw or the zero-mass fallback.
+  __device__ __forceinline__ double mass(float zp, float zq) const {
+    const double ap = (static_cast<double>(zp) - mp) * inv_t - log_sp;
     if (mode != kResidual) return exp_nonpos(ap);
-    const double aq = centered(q, v, mq, inv_t) - log_sq;
+    const double aq = (static_cast<double>(zq) - mq) * inv_t - log_sq;
     if (!(ap > aq)) return 0.0;  // P(v) <= Q(v): no residual mass, no exp needed
     return fmax(0.0, exp_nonpos(ap) - exp_nonpos(aq));
   }
 };
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void sample_lse_kernel(const VerifyArgs a) {
+__device__ __forceinline__ DrawRows<T> draw_rows_base(const VerifyArgs &a, const SampleState &st) {
+  DrawRows<T> d;
+  d.p = static_cast<const T *>(a.target) + static_cast<size_t>(st.tgt_row) * a.vocab;
+  d.q = static_cast<const T *>(a.draft) + static_cast<size_t>(st.drf_row) * a.vocab;
+  d.mp = st.max_p;
+  d.mq = st.max_q;
+  d.inv_t = a.inv_t;
+  d.log_sp = 0.0;
+  d.log_sq = 0.0;
+  d.mode = st.mode;
+  return d;
+}
+
+// The 8 masses of this thread's tokens in sample chunk c.
+template <typename T, bool VEC>
+__device__ __forceinline__ void chunk_masses(const DrawRows<T> &d, int c, int V, double (&mass)[kSampleElems]) {
+  const int v0 = c * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
+  float zp[kSampleElems], zq[kSampleElems];
+  load8<T, VEC>(d.p, v0, V, zp);
+  if (d.mode == kResidual) load8<T, VEC>(d.q, v0, V, zq);
+#pragma unroll
+  for (int k = 0; k < kSampleElems; ++k) mass[k] = d.mass(zp[k], d.mode == kResidual ? zq[k] : 0.f);
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void decide_lse_kernel(const VerifyArgs a) {
+  extern __shared__ __align__(16) unsigned char dyn_lds[];
+  __shared__ ReqRows rr;
+  __shared__ SampleState sh_state;
   __shared__ double sh_d[kWaves];
   const int i = blockIdx.y;
-  const SampleState st = a.state[i];
+  decide_request(a, i, reinterpret_cast<StatPartial *>(dyn_lds), rr, &sh_state, blockIdx.x == 0);
+  __syncthreads();
+  const SampleState st = sh_state;
   if (st.mode == kDone) return;
-  const int V = a.vocab;
-  const T *p = static_cast<const T *>(a.target) + static_cast<size_t>(st.tgt_row) * V;
-  const T *q = static_cast<const T *>(a.draft) + static_cast<size_t>(st.drf_row) * V;
-  const int begin = blockIdx.x * a.s_chunk_len;
-  const int end = min(begin + a.s_chunk_len, V);
+  const DrawRows<T> d = draw_rows_base<T>(a, st);
+  const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
+  float zp[kSampleElems], zq[kSampleElems];
+  load8<T, VEC>(d.p, v0, a.vocab, zp);
+  if (st.mode == kResidual) load8<T, VEC>(d.q, v0, a.vocab, zq);
   double sp = 0.0, sq = 0.0;
-  for (int v = begin + threadIdx.x; v < end; v += kThreads) {
-    sp += exp_nonpos(centered(p, v, st.max_p, a.inv_t));
-    if (st.mode == kResidual) sq += exp_nonpos(centered(q, v, st.max_q, a.inv_t));
+#pragma unroll
+  for (int k = 0; k < kSampleElems; ++k) {
+    sp += exp_nonpos((static_cast<double>(zp[k]) - st.max_p) * a.inv_t);
+    if (st.mode == kResidual) sq += exp_nonpos((static_cast<double>(zq[k]) - st.max_q) * a.inv_t);
   }
   sp = block_sum(sp, sh_d);
   sq = block_sum(sq, sh_d);
@@ -420,45 +509,47 @@ __global__ __launch_bounds__(kThreads) void sample_lse_kernel(const VerifyArgs a
   }
 }
 
+// log of the fp64 row sums from the lse partials (each thread owns up to 4 chunks).
 template <typename T>
-__device__ DrawRows<T> draw_rows(const VerifyArgs &a, const SampleState &st, int i, double *sh_d) {
-  double sp = 0.0, sq = 0.0;
+__device__ __forceinline__ void finish_draw_rows(const VerifyArgs &a, int i, DrawRows<T> &d, double *sh_d) {
+  constexpr int CPT = kMaxSampleChunks / kThreads;
   const double *src = a.lse_part + static_cast<size_t>(i) * a.s_chunks * 2;
-  for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
-    sp += src[2 * c];
-    sq += src[2 * c + 1];
+  double sp = 0.0, sq = 0.0;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = threadIdx.x + k * kThreads;
+    if (c < a.s_chunks) {
+      sp += src[2 * c];
+      sq += src[2 * c + 1];
+    }
   }
   sp = block_sum(sp, sh_d);
   sq = block_sum(sq, sh_d);
-  DrawRows<T> d;
-  d.p = static_cast<const T *>(a.target) + static_cast<size_t>(st.tgt_row) * a.vocab;
-  d.q = static_cast<const T *>(a.draft) + static_cast<size_t>(st.drf_row) * a.vocab;
-  d.mp = st.max_p;
-  d.mq = st.max_q;
-  d.inv_t = a.inv_t;
   d.log_sp = log(sp);
-  d.log_sq = st.mode == kResidual ? log(sq) : 0.0;
-  d.mode = st.mode;
-  return d;
+  d.log_sq = d.mode == kResidual ? log(sq) : 0.0;
 }
 
-template <typename T>
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void sample_mass_kernel(const VerifyArgs a) {
   __shared__ double sh_d[kWaves];
   const int i = blockIdx.y;
   const SampleState st = a.state[i];
   if (st.mode == kDone) return;
-  const DrawRows<T> d = draw_rows<T>(a, st, i, sh_d);
-  const int begin = blockIdx.x * a.s_chunk_len;
-  const int end = min(begin + a.s_chunk_len, a.vocab);
+  DrawRows<T> d = draw_rows_base<T>(a, st);
+  const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
+  float zp[kSampleElems], zq[kSampleElems];
+  load8<T, VEC>(d.p, v0, a.vocab, zp);  // issued before the partial sums are reduced
+  if (st.mode == kResidual) load8<T, VEC>(d.q, v0, a.vocab, zq);
+  finish_draw_rows(a, i, d, sh_d);
   double r = 0.0;
-  for (int v = begin + threadIdx.x; v < end; v += kThreads) r += d.mass(v);
+#pragma unroll
+  for (int k = 0; k < kSampleElems; ++k) r += d.mass(zp[k], st.mode == kResidual ? zq[k] : 0.f);
   r = block_sum(r, sh_d);
   if (threadIdx.x == 0) a.mass_part[static_cast<size_t>(i) * a.s_chunks + blockIdx.x] = r;
 }
 
 // Block-wide exclusive prefix sum of one double per thread (256 threads); also returns the total.
-__device__ double block_excl_scan(double v, double *sh, double *total) {
+__device__ __forceinline__ double block_excl_scan(double v, double *sh, double *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double incl = v;
   for (int o = 1; o < 64; o <<= 1) {
@@ -479,78 +570,87 @@ __device__ double block_excl_scan(double v, double *sh, double *total) {
   return off + excl;
 }
 
-// Inside [begin, end): the smallest v with offset + C(v) > target. Each thread owns one contiguous
-// run of tokens; the owner is the first thread whose inclusive prefix exceeds the target, and it
-// walks its run. If rounding leaves no crossing, the last token with positive mass is returned.
+// Inside sample chunk c, whose tokens start at cumulative mass `offset`: the smallest v with
+// offset + C(v) > target. Thread t owns tokens 8t..8t+7 of the chunk; the owner is the first
+// thread whose inclusive prefix exceeds the target, and it walks its 8 masses. If rounding leaves
+// no crossing, the last token with positive mass is returned.
 struct Found {
   int v;
   double c_v, c_prev;
 };
 
-template <typename T>
-__device__ Found scan_find(const DrawRows<T> &d, int begin, int end, double offset, double target,
-                           double *sh_scan, int *sh_int) {
-  __shared__ Found sh_found;
-  const int n = end - begin;
-  const int per = (n + kThreads - 1) / kThreads;
-  const int lo = begin + min(n, static_cast<int>(threadIdx.x) * per);
-  const int hi = begin + min(n, (static_cast<int>(threadIdx.x) + 1) * per);
+template <typename T, bool VEC>
+__device__ __forceinline__ Found chunk_find(const DrawRows<T> &d, int c, int V, double offset, double target, double *sh_scan,
+                            int *sh_int, Found *sh_found) {
+  double m[kSampleElems];
+  chunk_masses<T, VEC>(d, c, V, m);
   double local = 0.0;
-  for (int v = lo; v < hi; ++v) local += d.mass(v);
+#pragma unroll
+  for (int k = 0; k < kSampleElems; ++k) local += m[k];
   double total;
   const double start = offset + block_excl_scan(local, sh_scan, &total);
   const int me = static_cast<int>(threadIdx.x);
   const int owner = block_min_int(start + local > target ? me : INT_MAX, sh_int);
   const int last = -block_min_int(local > 0.0 ? -me : INT_MAX, sh_int);
   if (me == 0) {
-    sh_found.v = -1;
-    sh_found.c_v = offset;
-    sh_found.c_prev = offset;
+    sh_found->v = -1;
+    sh_found->c_v = offset;
+    sh_found->c_prev = offset;
   }
   __syncthreads();
   const bool is_owner = me == owner;
   if (is_owner || (owner == INT_MAX && me == last)) {
-    double c = start;
-    Found lastpos{-1, c, c};
-    Found hit{-1, c, c};
-    for (int v = lo; v < hi; ++v) {
-      const double prev = c;
-      const double m = d.mass(v);
-      c += m;
-      if (m > 0.0) lastpos = Found{v, c, prev};
-      if (is_owner && c > target) {
-        hit = Found{v, c, prev};
-        break;
+    const int v0 = c * kSampleChunk + me * kSampleElems;
+    double cum = start;
+    int last_v = -1, hit_v = -1;
+    double last_c = cum, last_p = cum, hit_c = cum, hit_p = cum;
+#pragma unroll
+    for (int k = 0; k < kSampleElems; ++k) {
+      const double prev = cum;
+      cum += m[k];
+      if (m[k] > 0.0) {
+        last_v = v0 + k;
+        last_c = cum;
+        last_p = prev;
+      }
+      if (is_owner && hit_v < 0 && cum > target) {
+        hit_v = v0 + k;
+        hit_c = cum;
+        hit_p = prev;
       }
     }
-    sh_found = hit.v >= 0 ? hit : lastpos;
+    const bool h = hit_v >= 0;
+    sh_found->v = h ? hit_v : last_v;
+    sh_found->c_v = h ? hit_c : last_c;
+    sh_found->c_prev = h ? hit_p : last_p;
   }
   __syncthreads();
-  const Found f = sh_found;
+  const Found f = *sh_found;
   __syncthreads();
   return f;
 }
 
-template <typename T>
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs a) {
   __shared__ double sh_d[kWaves];
   __shared__ int sh_i[kWaves];
   __shared__ double sh_cum[kMaxSampleChunks];
+  __shared__ Found sh_found;
   const int i = blockIdx.x;
   const SampleState st = a.state[i];
   if (st.mode == kDone) return;
-  DrawRows<T> d = draw_rows<T>(a, st, i, sh_d);
-  const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
-  // inclusive prefix of the chunk masses: each thread owns 4 consecutive chunks
+  // chunk masses (each thread owns 4 consecutive chunks), loaded together with the lse partials
   constexpr int CPT = kMaxSampleChunks / kThreads;
+  const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
   const int c0 = threadIdx.x * CPT;
   double mine[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) mine[k] = c0 + k < a.s_chunks ? mass[c0 + k] : 0.0;
+  DrawRows<T> d = draw_rows_base<T>(a, st);
+  finish_draw_rows(a, i, d, sh_d);
   double run = 0.0;
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    mine[k] = c0 + k < a.s_chunks ? mass[c0 + k] : 0.0;
-    run += mine[k];
-  }
+  for (int k = 0; k < CPT; ++k) run += mine[k];
   double z;
   double base = block_excl_scan(run, sh_d, &z);
 #pragma unroll
@@ -562,31 +662,36 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs 
   uint32_t fl = 0;
   Found f;
   if (!(z > 0.0)) {
-    // zero residual mass (not reachable in exact arithmetic): draw from P instead
+    // zero residual mass (not reachable in exact arithmetic): draw from P instead, chunk by chunk
     fl |= 4u;
     d.mode = kBonus;
-    double s = 0.0;
-    for (int v = threadIdx.x; v < a.vocab; v += kThreads) s += d.mass(v);
-    z = block_sum(s, sh_d);
-    f = scan_find(d, 0, a.vocab, 0.0, st.u * z, sh_d, sh_i);
-  } else {
+    double zp_tot = 0.0;
+    for (int c = 0; c < a.s_chunks; ++c) {
+      double m[kSampleElems];
+      chunk_masses<T, VEC>(d, c, a.vocab, m);
+      double t = 0.0;
+#pragma unroll
+      for (int k = 0; k < kSampleElems; ++k) t += m[k];
+      const double cs = block_sum(t, sh_d);
+      if (threadIdx.x == 0) sh_cum[c] = zp_tot + cs;  // inclusive prefix
+      zp_tot += cs;
+    }
+    z = zp_tot;
+    __syncthreads();
+  }
+  {
     const double target = st.u * z;
     int cand = INT_MAX, lastpos = -1;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int c = c0 + k;
-      if (c < a.s_chunks) {
-        if (cand == INT_MAX && sh_cum[c] > target) cand = c;
-        if (mine[k] > 0.0) lastpos = c;
-      }
+    for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
+      const double below = c > 0 ? sh_cum[c - 1] : 0.0;
+      if (cand == INT_MAX && sh_cum[c] > target) cand = c;
+      if (sh_cum[c] > below) lastpos = c;
     }
     const int c_star = block_min_int(cand, sh_i);
     const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
-    const int c = c_star != INT_MAX ? c_star : c_last;
+    const int c = c_star != INT_MAX ? c_star : max(c_last, 0);
     const double offset = c > 0 ? sh_cum[c - 1] : 0.0;
-    const int begin = c * a.s_chunk_len;
-    const int end = min(begin + a.s_chunk_len, a.vocab);
-    f = scan_find(d, begin, end, offset, target, sh_d, sh_i);
+    f = chunk_find<T, VEC>(d, c, a.vocab, offset, target, sh_d, sh_i, &sh_found);
   }
   if (threadIdx.x == 0) {
     const double target = st.u * z;
@@ -600,30 +705,26 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs 
 // host side
 // ------------------------------------------------------------------------------------------------
 struct VerifyPlan {
-  int chunks, chunk_len, s_chunks, s_chunk_len;
+  int chunks, chunk_len, s_chunks;
   size_t off_stats, off_state, off_lse, off_mass, total;
 };
 
 int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
   if (n_req < 1 || n_draft < 1 || n_draft > 63 || vocab < 1) return D3D_EINVAL;
-  const int rows = n_req * (2 * n_draft + 1);
-  int chunks = (kStatTargetBlocks + rows - 1) / rows;
-  chunks = std::max(1, std::min(chunks, (vocab + kStatMinChunk - 1) / kStatMinChunk));
+  const int rows_req = 2 * n_draft + 1;
+  const long long rows = static_cast<long long>(n_req) * rows_req;
+  if (rows > INT_MAX) return D3D_EINVAL;
+  const int s_chunks = (vocab + kSampleChunk - 1) / kSampleChunk;
+  if (s_chunks > kMaxSampleChunks) return D3D_EINVAL;
+  // One round of resident stats workgroups when the rows allow it; whole 64-token chunks; the
+  // request's partials must fit decide's LDS stage.
+  int chunks = static_cast<int>(std::max<long long>(1, kStatSlots / rows));
+  chunks = std::min(chunks, (vocab + kStatMinChunk - 1) / kStatMinChunk);
+  chunks = std::min(chunks, kMaxReqPartials / rows_req);
   int len = (vocab + chunks - 1) / chunks;
   len = (len + 63) / 64 * 64;
   p->chunk_len = len;
   p->chunks = (vocab + len - 1) / len;
-  int s_chunks = (kSampleTargetBlocks + n_req - 1) / n_req;
-  s_chunks = std::max(1, std::min(s_chunks, (vocab + kSampleMinChunk - 1) / kSampleMinChunk));
-  int s_len = (vocab + s_chunks - 1) / s_chunks;
-  s_len = (s_len + 63) / 64 * 64;
-  s_chunks = (vocab + s_len - 1) / s_len;
-  if (s_chunks > kMaxSampleChunks) {
-    s_len = (vocab + kMaxSampleChunks - 1) / kMaxSampleChunks;
-    s_len = (s_len + 63) / 64 * 64;
-    s_chunks = (vocab + s_len - 1) / s_len;
-  }
-  p->s_chunk_len = s_len;
   p->s_chunks = s_chunks;
   size_t off = 0;
   p->off_stats = off;
@@ -638,26 +739,23 @@ int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
   return D3D_OK;
 }
 
-template <typename T>
-int launch_verify(const VerifyArgs &a, bool vec, hipStream_t stream) {
-  const dim3 stat_grid(a.chunks, a.n_req * (2 * a.n_draft + 1));
-  if (a.greedy) {
-    if (vec)
-      stats_kernel<T, true, true><<<stat_grid, kThreads, 0, stream>>>(a);
-    else
-      stats_kernel<T, false, true><<<stat_grid, kThreads, 0, stream>>>(a);
-  } else {
-    if (vec)
-      stats_kernel<T, true, false><<<stat_grid, kThreads, 0, stream>>>(a);
-    else
-      stats_kernel<T, false, false><<<stat_grid, kThreads, 0, stream>>>(a);
-  }
-  decide_kernel<T><<<a.n_req, kDecideThreads, 0, stream>>>(a);
+template <typename T, bool VEC>
+int launch_verify(const VerifyArgs &a, hipStream_t stream) {
+  // greedy verify reads no draft rows
+  const int stat_rows = a.greedy ? a.n_tgt_rows : a.n_req * (2 * a.n_draft + 1);
+  const dim3 stat_grid(a.chunks, stat_rows);
+  if (a.greedy)
+    stats_kernel<T, VEC, true><<<stat_grid, kThreads, 0, stream>>>(a);
+  else
+    stats_kernel<T, VEC, false><<<stat_grid, kThreads, 0, stream>>>(a);
+  const int rows_req = a.greedy ? a.n_draft + 1 : 2 * a.n_draft + 1;
+  const size_t lds = sizeof(StatPartial) * static_cast<size_t>(rows_req) * a.chunks;
+  const dim3 d_grid(a.greedy ? 1 : a.s_chunks, a.n_req);
+  decide_lse_kernel<T, VEC><<<d_grid, kThreads, lds, stream>>>(a);
   if (!a.greedy) {
     const dim3 s_grid(a.s_chunks, a.n_req);
-    sample_lse_kernel<T><<<s_grid, kThreads, 0, stream>>>(a);
-    sample_mass_kernel<T><<<s_grid, kThreads, 0, stream>>>(a);
-    sample_pick_kernel<T><<<a.n_req, kThreads, 0, stream>>>(a);
+    sample_mass_kernel<T, VEC><<<s_grid, kThreads, 0, stream>>>(a);
+    sample_pick_kernel<T, VEC><<<a.n_req, kThreads, 0, stream>>>(a);
   }
   return launch_status();
 }
@@ -697,7 +795,6 @@ extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const voi
   a.chunks = p.chunks;
   a.chunk_len = p.chunk_len;
   a.s_chunks = p.s_chunks;
-  a.s_chunk_len = p.s_chunk_len;
   a.c_log2 = greedy ? 0.f : static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
   a.inv_t = greedy ? 0.0 : 1.0 / static_cast<double>(temperature);
   a.seed = seed;
@@ -718,5 +815,7 @@ extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const voi
   const bool aligned = (reinterpret_cast<uintptr_t>(target_logits) % 16 == 0) &&
                        (greedy || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
   const bool vec = aligned && (static_cast<size_t>(vocab) % width == 0);
-  return dtype == D3D_BF16 ? launch_verify<__bf16>(a, vec, stream) : launch_verify<float>(a, vec, stream);
+  if (dtype == D3D_BF16)
+    return vec ? launch_verify<__bf16, true>(a, stream) : launch_verify<__bf16, false>(a, stream);
+  return vec ? launch_verify<float, true>(a, stream) : launch_verify<float, false>(a, stream);
 }

@@ -158,3 +158,36 @@ def test_residual_token_differs_from_rejected_draft():
             p = special.softmax(inp["z_target"][i, j].astype(np.float64))
             q = special.softmax(inp["z_draft"][i, j].astype(np.float64))
             assert p[got["next_token"][i]] > q[got["next_token"][i]]
+
+
+def test_greedy_without_draft_logits():
+    """At T = 0 the draft logits are not read: NULL is accepted and gives the same outcome."""
+    require_gpu()
+    _say("verify: greedy with draft_logits = None")
+    base = synth.WORKLOADS["sync-bf16-L2048-V151936"]
+    w = synth.Workload("greedy-null", "bf16", 1, 1, 64, 16, 0, 0, (0,), 3, False, 32000, "zipf", 0.8, 0.0,
+                       4242, 0xBEEF)
+    inp = synth.verify_inputs(w)
+    for i in range(3):
+        cut = (5 * i + 2) % 16
+        inp["tokens"][i, :cut] = np.argmax(inp["z_target"][i, :cut], axis=-1)
+    got = _run(inp["z_target"], None, inp["tokens"], "bf16", 0.0, w.philox_seed, 1)
+    _compare(inp["z_target"], None, inp["tokens"], 0.0, w.philox_seed, 1, got, "greedy, no draft logits")
+    del base
+
+
+def test_masked_vocabulary_tail():
+    """Logits of -inf (a masked vocabulary tail that fills whole reduction chunks) carry no mass."""
+    require_gpu()
+    _say("verify: -inf logits over the vocabulary tail")
+    w = synth.Workload("masked", "bf16", 1, 1, 64, 8, 0, 0, (0,), 2, False, 32000, "zipf", 0.8, 1.0,
+                       99, 0xCAFE)
+    inp = synth.verify_inputs(w)
+    zt, zd = inp["z_target"].copy(), inp["z_draft"].copy()
+    zt[:, :, 27000:] = -np.inf
+    zd[:, :, 27000:] = -np.inf
+    tok = np.minimum(inp["tokens"], 26999).astype(np.int32)
+    for round_ in range(4):
+        got = _run(zt, zd, tok, "bf16", 1.0, w.philox_seed, round_)
+        assert np.all(got["next_token"] < 27000)
+        _compare(zt, zd, tok, 1.0, w.philox_seed, round_, got, f"masked tail round {round_}")
