@@ -9,9 +9,10 @@
 // touches one or two rows per request and is latency-bound, so it is built from few dependent
 // memory round trips):
 //   1. stats   grid (chunk, row), one round of resident workgroups: one coalesced 16-byte-vector
-//              pass over a slice of one logit row: running max (and first argmax), sum of
-//              exp((z - max)/T) with fp32 exp2 per element and fp64 accumulation per thread, and
-//              the logit at the row's draft token when the slice holds it. Partial per (row, chunk).
+//              pass over a slice of one logit row: sum of exp((z - ref)/T) against a reference
+//              logit of the slice with fp32 exp2 per element and fp64 accumulation per thread (the
+//              maximum and first argmax when greedy), and the logit at the row's draft token when
+//              the slice holds it. Partial per (row, chunk).
 //   2. decide + lse   grid (sample chunk, request): every workgroup stages its request's partials
 //              in LDS, merges each row in fp64, forms alpha_j from fp64 scalars, draws the Philox
 //              uniforms, finds the first rejection, S(k) and tau (the chunk-0 workgroup stores
@@ -45,7 +46,7 @@ constexpr int kMaxReqPartials = 2048;  // stats partials of one request staged i
 constexpr double kNear = 1e-6;
 
 struct StatPartial {
-  float max;
+  float max;    // greedy: the chunk maximum; sampling: the chunk's reference logit (see RowAcc)
   int32_t aux;  // greedy: first argmax; sampling: bits of the logit at the row's draft token when
                 // this chunk holds that token, else 0
   double sum;   // sum of exp((z - max) / T) over the chunk
@@ -87,13 +88,13 @@ struct VerifyArgs {
   double *mass_part;  // [n_req][s_chunks]
 };
 
-// exp(x) in fp64 for x <= 0, the only arguments produced here (differences from a running or row
-// maximum, or log-probabilities). Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software
+// exp(x) in fp64 for x < 709 (the arguments here are differences from a row reference, at most
+// about 84, or log-probabilities). Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software
 // Manual for the Elementary Functions", 1980): x = k ln2 + r with |r| <= ln2/2, ln2 split into a
 // 21-bit head (k * head is exact) and a tail; then the Taylor series of e^r to degree 12
 // (truncation below 2e-16 relative) and a scaling by 2^k. About 18 fp64 operations. NaN (from
 // -inf - -inf) and arguments below the smallest subnormal give 0.
-__device__ __forceinline__ double exp_nonpos(double x) {
+__device__ __forceinline__ double exp_fp64(double x) {
   constexpr double kInvLn2 = 1.4426950408889634;
   constexpr double kLn2Hi = 0.6931467056274414;      // ln 2 with its low 32 mantissa bits cleared
   constexpr double kLn2Lo = 4.7493250390316726e-07;  // ln 2 - kLn2Hi
@@ -156,19 +157,39 @@ __device__ __forceinline__ int block_min_int(int v, int *sh) {
 // ------------------------------------------------------------------------------------------------
 // 1. stats
 // ------------------------------------------------------------------------------------------------
+// Per-thread accumulator of one row slice. Greedy: the running maximum and its first index.
+// Sampling: a reference value m (an element of the slice) and s = sum of exp((z - m)/T) relative to
+// it. The reference is not kept at the running maximum element by element: a later logit above it
+// simply contributes a term above 1. It moves up to a group's maximum only when the fp32 sum of a
+// group's terms would leave the range (an exponent near 128), so every term stays below e^84 and
+// the reference itself contributes exactly 1. Consumers only need some reference, not the maximum.
 template <bool GREEDY>
 struct RowAcc {
   float m = -INFINITY;
   double s = 0.0;
   int arg = INT_MAX;
 
-  // Fold N consecutive elements starting at token index `idx` (z in fp32, exact for bf16).
   template <int N>
-  __device__ __forceinline__ void fold(const float (&z)[N], int idx, float c_log2, double inv_t) {
+  __device__ __forceinline__ static float group_max(const float (&z)[N]) {
     float vm = z[0];
 #pragma unroll
     for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);
+    return vm;
+  }
+
+  template <int N>
+  __device__ __forceinline__ static float group_sum(const float (&z)[N], float m, float c_log2) {
+    float part = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) part += __builtin_amdgcn_exp2f((z[k] - m) * c_log2);
+    return part;
+  }
+
+  // Fold N consecutive elements starting at token index `idx` (z in fp32, exact for bf16).
+  template <int N>
+  __device__ __forceinline__ void fold(const float (&z)[N], int idx, float c_log2, double inv_t) {
     if constexpr (GREEDY) {
+      const float vm = group_max(z);
       if (vm > m) {
         m = vm;
         int first = N - 1;
@@ -178,14 +199,18 @@ struct RowAcc {
         arg = idx + first;
       }
     } else {
-      if (vm > m) {
-        if (m != -INFINITY) s *= exp_nonpos((static_cast<double>(m) - vm) * inv_t);
+      if (m == -INFINITY) {  // no finite logit yet: the first finite group maximum is the reference
+        const float vm = group_max(z);
+        if (vm == -INFINITY) return;
         m = vm;
       }
-      if (m == -INFINITY) return;  // every logit so far is -inf: no mass yet
-      float part = 0.f;
-#pragma unroll
-      for (int k = 0; k < N; ++k) part += __builtin_amdgcn_exp2f((z[k] - m) * c_log2);
+      float part = group_sum(z, m, c_log2);
+      if (!(part < 0x1p120f)) {  // a logit far above the reference: move it to this group's max
+        const float vm = group_max(z);
+        s *= exp_fp64((static_cast<double>(m) - vm) * inv_t);
+        m = vm;
+        part = group_sum(z, m, c_log2);
+      }
       s += static_cast<double>(part);
     }
   }
@@ -273,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
     out.sum = 0.0;
   } else {
     const double mine =
-        acc.m == -INFINITY ? 0.0 : acc.s * exp_nonpos((static_cast<double>(acc.m) - m) * a.inv_t);
+        acc.m == -INFINITY ? 0.0 : acc.s * exp_fp64((static_cast<double>(acc.m) - m) * a.inv_t);
     out.sum = block_sum(mine, sh_d);
     out.aux = has_y ? __float_as_int(zy) : 0;
   }
@@ -336,18 +361,18 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
     for (int c = sub; c < C; c += g) {
       const StatPartial q = part[r * C + c];
       if (q.max > m) {
-        if (!a.greedy && m != -INFINITY) s *= exp_nonpos((static_cast<double>(m) - q.max) * a.inv_t);
+        if (!a.greedy && m != -INFINITY) s *= exp_fp64((static_cast<double>(m) - q.max) * a.inv_t);
         m = q.max;
         arg = q.aux;
       }
-      if (!a.greedy && q.max != -INFINITY) s += q.sum * exp_nonpos((static_cast<double>(q.max) - m) * a.inv_t);
+      if (!a.greedy && q.max != -INFINITY) s += q.sum * exp_fp64((static_cast<double>(q.max) - m) * a.inv_t);
     }
   }
   float wm = m;
   for (int o = g >> 1; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
   int warg = m == wm ? arg : INT_MAX;
   for (int o = g >> 1; o > 0; o >>= 1) warg = min(warg, __shfl_xor(warg, o));
-  double ws = m == -INFINITY ? 0.0 : s * exp_nonpos((static_cast<double>(m) - wm) * a.inv_t);
+  double ws = m == -INFINITY ? 0.0 : s * exp_fp64((static_cast<double>(m) - wm) * a.inv_t);
   for (int o = g >> 1; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
   if (sub == 0 && r < n_rows) {
     rr.max[r] = wm;
@@ -446,10 +471,10 @@ struct DrawRows {
   // max(0, P - Q) after a rejection, P for the bonus draw or the zero-mass fallback.
   __device__ __forceinline__ double mass(float zp, float zq) const {
     const double ap = (static_cast<double>(zp) - mp) * inv_t - log_sp;
-    if (mode != kResidual) return exp_nonpos(ap);
+    if (mode != kResidual) return exp_fp64(ap);
     const double aq = (static_cast<double>(zq) - mq) * inv_t - log_sq;
     if (!(ap > aq)) return 0.0;  // P(v) <= Q(v): no residual mass, no exp needed
-    return fmax(0.0, exp_nonpos(ap) - exp_nonpos(aq));
+    return fmax(0.0, exp_fp64(ap) - exp_fp64(aq));
   }
 };
 
@@ -497,8 +522,8 @@ __global__ __launch_bounds__(kThreads) void decide_lse_kernel(const VerifyArgs a
   double sp = 0.0, sq = 0.0;
 #pragma unroll
   for (int k = 0; k < kSampleElems; ++k) {
-    sp += exp_nonpos((static_cast<double>(zp[k]) - st.max_p) * a.inv_t);
-    if (st.mode == kResidual) sq += exp_nonpos((static_cast<double>(zq[k]) - st.max_q) * a.inv_t);
+    sp += exp_fp64((static_cast<double>(zp[k]) - st.max_p) * a.inv_t);
+    if (st.mode == kResidual) sq += exp_fp64((static_cast<double>(zq[k]) - st.max_q) * a.inv_t);
   }
   sp = block_sum(sp, sh_d);
   sq = block_sum(sq, sh_d);
