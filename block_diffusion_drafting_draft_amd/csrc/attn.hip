@@ -573,17 +573,18 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
   // this lane's query row (recomputed after the walk instead of held in registers)
   auto row_of = [&]() __attribute__((always_inline)) { return lane_row(a, it, wave * 32 + (lane & 31)); };
   bf16x8 qf[D / 16];
-  {
+  // Q fragments of this lane's row. They are loaded after the first tile copies are issued, and one
+  // full wait (which the compiler sees: otherwise it keeps Q pending into the loop and waits there
+  // for every copy in flight) then covers both, so the two latencies overlap.
+  auto load_q = [&]() __attribute__((always_inline)) {
     const LaneRow L = row_of();
     const __bf16 *qrow =
         static_cast<const __bf16 *>(a.q) + (static_cast<size_t>(R.q_begin + L.q_local) * a.Hq + L.h) * D;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
       qf[kk] = L.valid ? *reinterpret_cast<const bf16x8 *>(qrow + kk * 16 + hh * 8) : bf16x8{};
-  }
-  // Q has landed before the walk (a wait the compiler sees: otherwise it keeps Q pending into the
-  // loop and waits there for every copy in flight)
-  __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0);
+  };
   Rows1<D> st;
 #pragma unroll
   for (int b = 0; b < D / 32; ++b) st.o[b] = f32x16{};
@@ -704,7 +705,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
       issue(lds_k2, lds_v2, it.k0 + 2 * kKeys);
     }
     if (n_tiles > 3) load_pages(it.k0 + 3 * kKeys);
-    wait_next(-1);
+    load_q();  // every copy issued so far has landed too
+    barrier_keep_copies();
     for (int i = 0; i < n_full; i += kStages) {
       body(lds_k0, lds_v0, lds_k3, lds_v3, i);
       if (i + 1 < n_full) body(lds_k1, lds_v1, lds_k0, lds_v0, i + 1);
@@ -722,6 +724,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
       }
       __syncthreads();
     }
+  } else {
+    load_q();
   }
 
   // ---- in-pack tail (first split only) ----
@@ -909,18 +913,33 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
   const int q_local = local / a.Hq, h = local - q_local * a.Hq;
   const size_t stride = static_cast<size_t>(R.n_q) * a.Hq;  // slots between consecutive splits
   const size_t slot0 = static_cast<size_t>(R.part_begin) + static_cast<size_t>(q_local) * a.Hq + h;
+  // every partial is loaded up front (one round trip), then merged in split order
+  const int ns = R.n_splits;
+  float pm[kMaxSplits], pl[kMaxSplits];
+  f32x4 po[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    pm[s] = -INFINITY;
+    pl[s] = 0.f;
+    po[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s < ns) {
+      const size_t slot = slot0 + s * stride;
+      pm[s] = a.part_ml[slot * 2];
+      pl[s] = a.part_ml[slot * 2 + 1];
+      po[s] = *reinterpret_cast<const f32x4 *>(a.part_o + slot * D + d0);
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < R.n_splits; ++s) M = fmaxf(M, a.part_ml[(slot0 + s * stride) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, pm[s]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < R.n_splits; ++s) {
-    const size_t slot = slot0 + s * stride;
-    const float wgt = __builtin_amdgcn_exp2f(a.part_ml[slot * 2] - M);
-    lsum += wgt * a.part_ml[slot * 2 + 1];
-    const f32x4 o = *reinterpret_cast<const f32x4 *>(a.part_o + slot * D + d0);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] += wgt * o[k];
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const float wgt = s < ns ? __builtin_amdgcn_exp2f(pm[s] - M) : 0.f;
+    lsum += wgt * pl[s];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] += wgt * po[s][k];
   }
   const float inv = 1.f / lsum;
   const size_t orow = static_cast<size_t>(R.q_begin + q_local) * a.Hq + h;
