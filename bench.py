@@ -4,18 +4,21 @@
 A step is one pass of the whole hot path over one synthetic round of the async workload
 (B = 16, C = 12, F = 2: 24 blocks, 384 packed queries; 32 query / 8 key-value heads, head dim 128,
 4096-token prefix; verify of 16 target + 15 draft rows over a 151936-token vocabulary):
-  1. branch descriptors built on the host and copied to the GPU from pinned memory,
+  1. branch descriptors of every request built on the host (one batched call) into pinned memory and
+     copied to the GPU,
   2. draft_attn_packed (one drafter attention layer, all heads),
-  3. spec_verify (stats, decide, residual / bonus sample),
+  3. spec_verify (stats, decide + lse, residual / bonus mass, pick),
   4. branch_cache_match.
 Inputs are resident in HBM before the timed region. The device part of a step (2-4) is captured
 once in a HIP graph, with 2 and 3 on two streams (they are independent within a round: drafting the
-next block's branches overlaps verifying the current block) joined before 4; each step builds its descriptors on the host into a ring of pinned buffers,
-enqueues their copy and replays the graph. W untimed warm-up steps, then K timed steps between
-device synchronisations. Per-call durations come from HIP events recorded on the launch stream
-around K replays of a graph holding only that call. Prints one JSON line.
+next block's branches overlaps verifying the current block) joined before 4; each step builds its
+descriptors on the host into a ring of pinned buffers, enqueues their copy and replays the graph.
+W untimed warm-up steps, then K timed steps between device synchronisations. Per-call durations
+come from HIP events recorded on the launch stream around K replays of a graph holding only that
+call. Prints one JSON line. `--call NAME` replays only that call's graph (the command to profile one
+call's kernels alone).
 
-`python bench.py --gpus N --steps K --warmup W [--workload NAME] [--no-cpu-baseline]`
+`python bench.py --gpus N --steps K --warmup W [--workload NAME] [--no-cpu-baseline] [--call NAME]`
 """
 
 import argparse
@@ -44,6 +47,9 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match"), default=None,
+                   help="only replay this call's graph (warmup + steps times, nothing else on the GPU) and print "
+                        "its event-timed duration: the command to profile one call's kernels alone")
     return p.parse_args()
 
 
@@ -247,6 +253,20 @@ def main():
         graphs[name] = g
     torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
+    if args.call:
+        g = graphs[args.call]
+        for _ in range(args.warmup):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(cur)
+        for _ in range(args.steps):
+            g.replay()
+        e1.record(cur)
+        e1.synchronize()
+        print(json.dumps({"workload": w.name, "call": args.call, "replays": args.steps,
+                          "us_per_call": round(e0.elapsed_time(e1) * 1e3 / max(args.steps, 1), 3)}), flush=True)
+        return 0
 
     def step(k):
         slot = k % len(ring)
