@@ -422,7 +422,7 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
     SampleState st;
     st.pad = 0;
     st.tgt_row = i * (nd + 1) + n_acc;
-    st.drf_row = i * nd + min(n_acc, nd - 1);  // never read in bonus mode
+    st.drf_row = i * nd + min(n_acc, nd - 1);  // a valid row in every mode; its values unused for the bonus
     st.max_p = rr.max[n_acc];
     st.max_q = (!a.greedy && n_acc < nd) ? rr.max[nd + 1 + n_acc] : 0.f;
     st.u = philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
@@ -432,8 +432,11 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
       a.n_acc[i] = n_acc;
       if (a.tau) a.tau[i] = static_cast<float>(1.0 + tsum);
       if (a.flags) a.flags[i] = near ? 1u : 0u;
-      if (a.greedy) a.next_token[i] = rr.arg[n_acc];
-      else a.state[i] = st;
+      if (a.greedy) {
+        a.next_token[i] = rr.arg[n_acc];
+      } else {
+        a.state[i] = st;
+      }
     }
   }
 }
@@ -442,21 +445,34 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
 // 2.-4. fp64 sample of the one row the next token is drawn from
 // ------------------------------------------------------------------------------------------------
 // Eight consecutive logits from token v0 on; tokens past the vocabulary read as -inf (zero mass).
+// The loads are unconditional (from a clamped, in-bounds position) and the masking is a select
+// afterwards, so a caller's loads of several rows all issue before the first wait. Vector mode
+// needs V >= 8 and V a multiple of the vector width (16 B); then a partial group can only occur for
+// fp32 (4 per vector) with v0 = V - 4, where the clamped load starts 4 tokens early.
 template <typename T, bool VEC>
 __device__ __forceinline__ void load8(const T *row, int v0, int V, float (&z)[kSampleElems]) {
-  if (VEC && v0 + kSampleElems <= V) {
+  if constexpr (VEC) {
     constexpr int W = 16 / sizeof(T);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(row + v0);
+    const int vc = min(v0, V - kSampleElems);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(row + vc);
+    float t[kSampleElems];
 #pragma unroll
     for (int h = 0; h < kSampleElems / W; ++h) {
-      float t[W];
-      unpack(vp[h], t, static_cast<const T *>(nullptr));
+      float u[W];
+      unpack(vp[h], u, static_cast<const T *>(nullptr));
 #pragma unroll
-      for (int k = 0; k < W; ++k) z[h * W + k] = t[k];
+      for (int k = 0; k < W; ++k) t[h * W + k] = u[k];
     }
+    const bool shifted = vc != v0;
+#pragma unroll
+    for (int k = 0; k < kSampleElems; ++k)
+      z[k] = v0 + k < V ? (shifted ? t[(k + 4) & (kSampleElems - 1)] : t[k]) : -INFINITY;
   } else {
 #pragma unroll
-    for (int k = 0; k < kSampleElems; ++k) z[k] = v0 + k < V ? load_elem(row + v0 + k) : -INFINITY;
+    for (int k = 0; k < kSampleElems; ++k) {
+      const float t = load_elem(row + min(v0 + k, V - 1));
+      z[k] = v0 + k < V ? t : -INFINITY;
+    }
   }
 }
 
@@ -498,7 +514,7 @@ __device__ __forceinline__ void chunk_masses(const DrawRows<T> &d, int c, int V,
   const int v0 = c * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
   float zp[kSampleElems], zq[kSampleElems];
   load8<T, VEC>(d.p, v0, V, zp);
-  if (d.mode == kResidual) load8<T, VEC>(d.q, v0, V, zq);
+  load8<T, VEC>(d.q, v0, V, zq);  // unconditional: both loads issue before the first wait
 #pragma unroll
   for (int k = 0; k < kSampleElems; ++k) mass[k] = d.mass(zp[k], d.mode == kResidual ? zq[k] : 0.f);
 }
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void decide_lse_kernel(const VerifyArgs a
   const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
   float zp[kSampleElems], zq[kSampleElems];
   load8<T, VEC>(d.p, v0, a.vocab, zp);
-  if (st.mode == kResidual) load8<T, VEC>(d.q, v0, a.vocab, zq);
+  load8<T, VEC>(d.q, v0, a.vocab, zq);  // the draft row is valid in every mode
   double sp = 0.0, sq = 0.0;
 #pragma unroll
   for (int k = 0; k < kSampleElems; ++k) {
@@ -541,36 +557,17 @@ __device__ __forceinline__ void finish_draw_rows(const VerifyArgs &a, int i, Dra
   const double *src = a.lse_part + static_cast<size_t>(i) * a.s_chunks * 2;
   double sp = 0.0, sq = 0.0;
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
+  for (int k = 0; k < CPT; ++k) {  // unconditional loads (clamped), then selects
     const int c = threadIdx.x + k * kThreads;
-    if (c < a.s_chunks) {
-      sp += src[2 * c];
-      sq += src[2 * c + 1];
-    }
+    const int cc = min(c, a.s_chunks - 1);
+    const double vp = src[2 * cc], vq = src[2 * cc + 1];
+    sp += c < a.s_chunks ? vp : 0.0;
+    sq += c < a.s_chunks ? vq : 0.0;
   }
   sp = block_sum(sp, sh_d);
   sq = block_sum(sq, sh_d);
   d.log_sp = log(sp);
   d.log_sq = d.mode == kResidual ? log(sq) : 0.0;
-}
-
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_mass_kernel(const VerifyArgs a) {
-  __shared__ double sh_d[kWaves];
-  const int i = blockIdx.y;
-  const SampleState st = a.state[i];
-  if (st.mode == kDone) return;
-  DrawRows<T> d = draw_rows_base<T>(a, st);
-  const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
-  float zp[kSampleElems], zq[kSampleElems];
-  load8<T, VEC>(d.p, v0, a.vocab, zp);  // issued before the partial sums are reduced
-  if (st.mode == kResidual) load8<T, VEC>(d.q, v0, a.vocab, zq);
-  finish_draw_rows(a, i, d, sh_d);
-  double r = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSampleElems; ++k) r += d.mass(zp[k], st.mode == kResidual ? zq[k] : 0.f);
-  r = block_sum(r, sh_d);
-  if (threadIdx.x == 0) a.mass_part[static_cast<size_t>(i) * a.s_chunks + blockIdx.x] = r;
 }
 
 // Block-wide exclusive prefix sum of one double per thread (256 threads); also returns the total.
@@ -655,24 +652,20 @@ __device__ __forceinline__ Found chunk_find(const DrawRows<T> &d, int c, int V, 
   return f;
 }
 
+// The draw of request i from its chunk masses: chunk prefix, the chunk holding u'Z, then the
+// in-chunk scan.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs a) {
-  __shared__ double sh_d[kWaves];
-  __shared__ int sh_i[kWaves];
-  __shared__ double sh_cum[kMaxSampleChunks];
-  __shared__ Found sh_found;
-  const int i = blockIdx.x;
-  const SampleState st = a.state[i];
-  if (st.mode == kDone) return;
-  // chunk masses (each thread owns 4 consecutive chunks), loaded together with the lse partials
-  constexpr int CPT = kMaxSampleChunks / kThreads;
+__device__ __forceinline__ void draw_token(const VerifyArgs &a, int i, const SampleState &st, DrawRows<T> d,
+                                           double *sh_d, int *sh_i, double *sh_cum, Found *sh_found) {
+  constexpr int CPT = kMaxSampleChunks / kThreads;  // each thread owns 4 consecutive chunks
   const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
   const int c0 = threadIdx.x * CPT;
   double mine[CPT];
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) mine[k] = c0 + k < a.s_chunks ? mass[c0 + k] : 0.0;
-  DrawRows<T> d = draw_rows_base<T>(a, st);
-  finish_draw_rows(a, i, d, sh_d);
+  for (int k = 0; k < CPT; ++k) {
+    const double v = mass[min(c0 + k, a.s_chunks - 1)];  // unconditional (clamped), then a select
+    mine[k] = c0 + k < a.s_chunks ? v : 0.0;
+  }
   double run = 0.0;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) run += mine[k];
@@ -685,7 +678,6 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs 
   }
   __syncthreads();
   uint32_t fl = 0;
-  Found f;
   if (!(z > 0.0)) {
     // zero residual mass (not reachable in exact arithmetic): draw from P instead, chunk by chunk
     fl |= 4u;
@@ -704,26 +696,58 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs 
     z = zp_tot;
     __syncthreads();
   }
-  {
-    const double target = st.u * z;
-    int cand = INT_MAX, lastpos = -1;
-    for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
-      const double below = c > 0 ? sh_cum[c - 1] : 0.0;
-      if (cand == INT_MAX && sh_cum[c] > target) cand = c;
-      if (sh_cum[c] > below) lastpos = c;
-    }
-    const int c_star = block_min_int(cand, sh_i);
-    const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
-    const int c = c_star != INT_MAX ? c_star : max(c_last, 0);
-    const double offset = c > 0 ? sh_cum[c - 1] : 0.0;
-    f = chunk_find<T, VEC>(d, c, a.vocab, offset, target, sh_d, sh_i, &sh_found);
+  const double target = st.u * z;
+  int cand = INT_MAX, lastpos = -1;
+  for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
+    const double below = c > 0 ? sh_cum[c - 1] : 0.0;
+    if (cand == INT_MAX && sh_cum[c] > target) cand = c;
+    if (sh_cum[c] > below) lastpos = c;
   }
+  const int c_star = block_min_int(cand, sh_i);
+  const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
+  const int c = c_star != INT_MAX ? c_star : max(c_last, 0);
+  const double offset = c > 0 ? sh_cum[c - 1] : 0.0;
+  const Found f = chunk_find<T, VEC>(d, c, a.vocab, offset, target, sh_d, sh_i, sh_found);
   if (threadIdx.x == 0) {
-    const double target = st.u * z;
     if (fabs(target - f.c_v) < kNear * z || fabs(target - f.c_prev) < kNear * z) fl |= 2u;
     a.next_token[i] = f.v;
     if (a.flags) a.flags[i] |= fl;
   }
+}
+
+// Residual (or bonus) mass of one 2048-token chunk.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_mass_kernel(const VerifyArgs a) {
+  __shared__ double sh_d[kWaves];
+  const int i = blockIdx.y;
+  const SampleState st = a.state[i];
+  if (st.mode == kDone) return;
+  DrawRows<T> d = draw_rows_base<T>(a, st);
+  const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
+  float zp[kSampleElems], zq[kSampleElems];
+  load8<T, VEC>(d.p, v0, a.vocab, zp);  // issued before the partial sums are reduced
+  load8<T, VEC>(d.q, v0, a.vocab, zq);  // the draft row is valid in every mode
+  finish_draw_rows(a, i, d, sh_d);
+  double r = 0.0;
+#pragma unroll
+  for (int k = 0; k < kSampleElems; ++k) r += d.mass(zp[k], zq[k]);
+  r = block_sum(r, sh_d);
+  if (threadIdx.x == 0) a.mass_part[static_cast<size_t>(i) * a.s_chunks + blockIdx.x] = r;
+}
+
+// One workgroup per request: the draw from the published chunk masses.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs a) {
+  __shared__ double sh_d[kWaves];
+  __shared__ int sh_i[kWaves];
+  __shared__ double sh_cum[kMaxSampleChunks];
+  __shared__ Found sh_found;
+  const int i = blockIdx.x;
+  const SampleState st = a.state[i];
+  if (st.mode == kDone) return;
+  DrawRows<T> d = draw_rows_base<T>(a, st);
+  finish_draw_rows(a, i, d, sh_d);
+  draw_token<T, VEC>(a, i, st, d, sh_d, sh_i, sh_cum, &sh_found);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -839,7 +863,7 @@ extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const voi
   const size_t width = 16 / esize;
   const bool aligned = (reinterpret_cast<uintptr_t>(target_logits) % 16 == 0) &&
                        (greedy || reinterpret_cast<uintptr_t>(draft_logits) % 16 == 0);
-  const bool vec = aligned && (static_cast<size_t>(vocab) % width == 0);
+  const bool vec = aligned && (static_cast<size_t>(vocab) % width == 0) && vocab >= kSampleElems;
   if (dtype == D3D_BF16)
     return vec ? launch_verify<__bf16, true>(a, stream) : launch_verify<__bf16, false>(a, stream);
   return vec ? launch_verify<float, true>(a, stream) : launch_verify<float, false>(a, stream);
