@@ -194,9 +194,18 @@ def cpu_baseline(w, budget_s):
                                       vin["philox_seed"], 0, i)
             match.match_request(blocks, o.n_accepted, o.next_token)
         times.append(time.perf_counter() - t0)
-    threads = max([p["num_threads"] for p in threadpool_info()] or [1])
+    info = threadpool_info()
+    threads = max([p["num_threads"] for p in info] or [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=statistics.median(times) * 1e6, unit="µs per packed draft round", cores=threads,
-                kind="oracle",
+                kind="oracle", cpu_model=model, cpu_count=os.cpu_count(),
+                affinity=len(os.sched_getaffinity(0)),
+                blas=sorted({f"{p.get('internal_api')} {p.get('version')}" for p in info if p.get("user_api") == "blas"}),
                 sample=f"{len(times)} full rounds of the same workload (all queries and heads, verify of every row, "
                        f"match), float64 NumPy, median; not a tuned CPU implementation")
 
@@ -286,9 +295,29 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    def call_us(name, reps):
-        g = graphs[name]
-        for _ in range(5):
+    def per_replay_us(g, reps, warmup=10, before=None):
+        """HIP-event duration (µs) of each of `reps` replays of graph g on the launch stream, after
+        `warmup` untimed replays; `before(k)`, if given, is enqueued (untimed) ahead of replay k."""
+        for _ in range(warmup):
+            g.replay()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for k, (e0, e1) in enumerate(evs):
+            if before is not None:
+                before(k)
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+        torch.cuda.synchronize()
+        return np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+
+    def summary(x):
+        return float(np.median(x)), float(np.percentile(x, 10)), float(np.percentile(x, 90))
+
+    def mean_us(g, reps, warmup=10):
+        """Average duration (µs) of `reps` back-to-back replays of graph g between two HIP events on
+        the launch stream: the per-launch time a kernel profiler reports, launch latency amortised."""
+        for _ in range(warmup):
             g.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -299,10 +328,30 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
-    reps = max(args.steps, 20)
-    t_attn, t_ver, t_match = call_us("draft_attn_packed", reps), call_us("spec_verify", reps), \
-        call_us("branch_cache_match", reps)
-    t_round = call_us("round", reps)
+    reps = 100
+    names = ("draft_attn_packed", "spec_verify", "branch_cache_match", "round")
+    t_attn, t_ver, t_match, t_round = (mean_us(graphs[n], reps) for n in names)
+    stats = {n: summary(per_replay_us(graphs[n], reps)) for n in names}
+    # cold verify: before every timed call the MALL is flushed by reading 512 MiB (untimed; a read
+    # leaves no dirty lines whose write-back would compete with the timed reads), and the logits
+    # rotate over three copies
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    copies = [(r.z_t.clone(), r.z_d.clone(), r.tokens.clone()) for _ in range(3)]
+    cold_graphs = []
+    for zt, zd, tok in copies:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            r.lib.spec_verify(zt, zd, tok, r.vin["temperature"], r.vin["philox_seed"], r.round, ws=r.ver_ws,
+                              out=r.ver_out)
+        cold_graphs.append(g)
+    torch.cuda.synchronize()
+    cold = []
+    for k in range(reps):
+        torch.sum(flush, dim=0, out=sink)
+        cold.append(per_replay_us(cold_graphs[k % 3], 1, warmup=0)[0])
+    t_ver_cold = summary(np.array(cold))
+    del flush, sink, copies, cold_graphs
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(cur)
@@ -343,10 +392,22 @@ def main():
         "calls_us": {"descriptor_copy": round(t_desc, 3), "draft_attn_packed": round(t_attn, 3),
                      "spec_verify": round(t_ver, 3), "branch_cache_match": round(t_match, 3),
                      "device_round": round(t_round, 3)},
+        "calls_us_median_p10_p90": {("device_round" if n == "round" else n): [round(v[0], 3), round(v[1], 3),
+                                                                              round(v[2], 3)]
+                                    for n, v in stats.items()},
+        "timing": "calls_us: mean of 100 back-to-back graph replays between two HIP events on the launch "
+                  "stream after 10 warm-up replays (used for the percentages and the roofline); "
+                  "calls_us_median_p10_p90: HIP events around each of 100 replays (includes each launch's "
+                  "latency)",
         "attn": {"tflops": round(attn_tflops, 2), "pct_mfma_peak": round(100 * attn_tflops / peak, 2),
                  "flops": attn_flops, "bytes": attn_bytes},
         "verify": {"gbs": round(ver_gbs, 1), "pct_hbm_peak": round(100 * ver_gbs / HBM_PEAK_GBS, 2),
                    "bytes": ver_bytes},
+        "verify_cold": {"us": round(t_ver_cold[0], 3), "p10_p90": [round(t_ver_cold[1], 3), round(t_ver_cold[2], 3)],
+                        "gbs": round(ver_bytes / (t_ver_cold[0] * 1e-6) / 1e9, 1),
+                        "pct_hbm_peak": round(100 * ver_bytes / (t_ver_cold[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                        "protocol": "512 MiB read before each call (untimed) to flush the MALL; logits rotate "
+                                    "over 3 copies; HIP events around each call; median of 100"},
         "roofline": {"bound": "mfma", "kernel": "draft_attn_packed (attn_kernel + combine_kernel)",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},

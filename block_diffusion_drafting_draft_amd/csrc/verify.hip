@@ -39,6 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStatSlots = 2048;  // stats workgroups resident at once: 8 per CU on 256 CUs
 constexpr int kStatMinChunk = 1024;
+constexpr int kStatMaxChunks = 32;  // per row: more would only lengthen decide's row merge
 constexpr int kSampleElems = 8;                        // tokens per thread in the sample passes
 constexpr int kSampleChunk = kThreads * kSampleElems;  // tokens per sample workgroup
 constexpr int kMaxSampleChunks = 1024;
@@ -354,25 +355,30 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
   int g = 64;
   while (g > 1 && n_rows * g > kThreads) g >>= 1;
   const int r = threadIdx.x / g, sub = threadIdx.x % g;
+  // the row's maximum reference (and, greedy, the first argmax: chunks are visited in increasing
+  // order per lane and ties go to the lowest index), then one independent exp per chunk
   float m = -INFINITY;
   int arg = INT_MAX;
-  double s = 0.0;
   if (r < n_rows) {
     for (int c = sub; c < C; c += g) {
       const StatPartial q = part[r * C + c];
       if (q.max > m) {
-        if (!a.greedy && m != -INFINITY) s *= exp_fp64((static_cast<double>(m) - q.max) * a.inv_t);
         m = q.max;
         arg = q.aux;
       }
-      if (!a.greedy && q.max != -INFINITY) s += q.sum * exp_fp64((static_cast<double>(q.max) - m) * a.inv_t);
     }
   }
   float wm = m;
   for (int o = g >> 1; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
   int warg = m == wm ? arg : INT_MAX;
   for (int o = g >> 1; o > 0; o >>= 1) warg = min(warg, __shfl_xor(warg, o));
-  double ws = m == -INFINITY ? 0.0 : s * exp_fp64((static_cast<double>(m) - wm) * a.inv_t);
+  double ws = 0.0;
+  if (!a.greedy && r < n_rows && wm != -INFINITY) {
+    for (int c = sub; c < C; c += g) {
+      const StatPartial q = part[r * C + c];
+      if (q.max != -INFINITY) ws += q.sum * exp_fp64((static_cast<double>(q.max) - wm) * a.inv_t);
+    }
+  }
   for (int o = g >> 1; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
   if (sub == 0 && r < n_rows) {
     rr.max[r] = wm;
@@ -394,10 +400,10 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
     if (a.greedy) {
       alpha = (rr.tok[j] == rr.arg[j]) ? 1.0 : 0.0;
     } else {
-      const double lp = (static_cast<double>(rr.zy[j]) - rr.max[j]) * a.inv_t - log(rr.sum[j]);
-      const double lq = (static_cast<double>(rr.zy[nd + 1 + j]) - rr.max[nd + 1 + j]) * a.inv_t -
-                        log(rr.sum[nd + 1 + j]);
-      const double py = exp(lp), qy = exp(lq);
+      // P_j(y) = exp((z_y - ref)/T) / sum_j, likewise Q_j(y)
+      const double py = exp_fp64((static_cast<double>(rr.zy[j]) - rr.max[j]) * a.inv_t) / rr.sum[j];
+      const double qy =
+          exp_fp64((static_cast<double>(rr.zy[nd + 1 + j]) - rr.max[nd + 1 + j]) * a.inv_t) / rr.sum[nd + 1 + j];
       alpha = qy > 0.0 ? fmin(1.0, py / qy) : 1.0;
     }
     u = philox_uniform(a.seed, static_cast<uint32_t>(j), static_cast<uint32_t>(i), a.round, 0u);
@@ -770,6 +776,7 @@ int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
   int chunks = static_cast<int>(std::max<long long>(1, kStatSlots / rows));
   chunks = std::min(chunks, (vocab + kStatMinChunk - 1) / kStatMinChunk);
   chunks = std::min(chunks, kMaxReqPartials / rows_req);
+  chunks = std::min(chunks, kStatMaxChunks);
   int len = (vocab + chunks - 1) / chunks;
   len = (len + 63) / 64 * 64;
   p->chunk_len = len;
