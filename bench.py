@@ -412,10 +412,61 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},
     }
+    out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def next_row_topk(r, torch, cur, mean_us):
+    """Drafter token selection (the first next row, not part of the step): greedy tokens of every
+    masked position of the packed blocks (k = 1 over rows of drafter logits; synthetic N(0, 3) bf16
+    logits drawn on the device: timing only) and the branch anchors in the builder's layout (top-F of
+    draft rows 1..C-1 excluding the drafts, then the full-accept anchor). HBM bytes = rows x V x 2."""
+    w, lib = r.w, r.lib
+    if not w.coverage or w.dtype != "bf16":
+        return None
+    B, C, F, V = r.B, w.coverage, w.fanout, w.vocab
+    n_pos = int(r.q.shape[0])
+    gen = torch.Generator(device="cuda").manual_seed(w.seed)
+    logits = (torch.randn((n_pos, V), generator=gen, device="cuda") * 3.0).to(torch.bfloat16)
+    masked = torch.tensor([p for p in range(n_pos) if p % B != 0], dtype=torch.int32, device="cuda")
+    toks = torch.empty((masked.numel(), 1), dtype=torch.int32, device="cuda")
+    n_req, nd = r.tokens.shape
+    per = (C - 1) * F + 1
+    rows = torch.tensor([i * nd + k - 1 for i in range(n_req) for k in range(1, C)], dtype=torch.int32, device="cuda")
+    excl = r.tokens[:, :C - 1].reshape(-1).contiguous()
+    offs = torch.tensor([i * per + (k - 1) * F for i in range(n_req) for k in range(1, C)], dtype=torch.int32,
+                        device="cuda")
+    offs_full = torch.arange(n_req, dtype=torch.int32, device="cuda") * per + (C - 1) * F
+    z_next = r.z_d[:, nd - 1].contiguous()  # stands in for the row after the block
+    alt = torch.empty((n_req, per), dtype=torch.int32, device="cuda")
+    zd_rows = r.z_d.reshape(n_req * nd, V)
+    ws_t = torch.empty(lib.draft_topk_workspace(masked.numel(), V, 1), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(lib.draft_topk_workspace(rows.numel(), V, F), lib.draft_topk_workspace(n_req, V, 1)),
+                       dtype=torch.uint8, device="cuda")
+
+    def tokens():
+        lib.draft_topk(logits, 1, rows=masked, out=toks, ws=ws_t)
+
+    def anchors():
+        lib.draft_topk(zd_rows, F, rows=rows, exclude=excl, out=alt, out_off=offs, ws=ws_a)
+        lib.draft_topk(z_next, 1, out=alt, out_off=offs_full, ws=ws_a)
+
+    res = {}
+    for name, fn, n_rows in (("tokens", tokens, masked.numel()), ("anchors", anchors, rows.numel() + n_req)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        t = mean_us(g, 100)
+        nbytes = n_rows * V * 2
+        res[name] = {"rows": int(n_rows), "us": round(t, 3), "gbs": round(nbytes / (t * 1e-6) / 1e9, 1),
+                     "pct_hbm_peak": round(100 * nbytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+    del logits
+    return res
 
 
 def _kernel_digest():

@@ -41,6 +41,9 @@ _SIGNATURES = {
                                _c.c_size_t, _c.c_void_p]),
     "branch_cache_match": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "draft_topk_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
+    "draft_topk": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int,
+                              _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "d3d_status_string": (_c.c_char_p, [_c.c_int]),
 }
 EXPORTS = tuple(_SIGNATURES)
@@ -269,3 +272,37 @@ def branch_cache_match(descs, req_block_off, n_accepted, next_token, hit=None, s
                                    _ptr(next_token), _ptr(hit), _stream(stream))
     _check(st, "branch_cache_match")
     return hit
+
+
+def draft_topk_workspace(n_rows, vocab, k):
+    return int(load().draft_topk_workspace(n_rows, vocab, k))
+
+
+def draft_topk(logits, k, rows=None, exclude=None, out=None, out_off=None, n_rows=None, ws=None, stream=None):
+    """The k best tokens of logit rows (larger logit first, ties to the lower id), skipping exclude[r].
+    logits [rows_in, V] on the GPU; rows / exclude / out_off: int32 GPU tensors or None. Returns out
+    (int32 [n_rows, k] when allocated here)."""
+    _dev(logits, "logits")
+    dt = _dtype_code(logits)
+    vocab = logits.shape[-1]
+    for t, n in ((rows, "rows"), (exclude, "exclude"), (out_off, "out_off")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.int32:
+                raise TypeError(f"{n} must be int32")
+    if n_rows is None:
+        n_rows = rows.numel() if rows is not None else logits.numel() // vocab
+    if out is None:
+        if out_off is not None:
+            raise ValueError("pass out together with out_off")
+        out = torch.empty((n_rows, k), dtype=torch.int32, device=logits.device)
+    _dev(out, "out")
+    need = draft_topk_workspace(n_rows, vocab, k)
+    if need == 0:
+        raise ValueError("unsupported draft_topk shape")
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    st = load().draft_topk(dt, _ptr(logits), vocab, n_rows, _ptr(rows), _ptr(exclude), k, _ptr(out), _ptr(out_off),
+                           _ptr(ws), need, _stream(stream))
+    _check(st, "draft_topk")
+    return out

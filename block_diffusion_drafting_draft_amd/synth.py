@@ -175,6 +175,7 @@ def verify_inputs(w, n_req=None, vocab=None, block_size=None, seed=None, tempera
                 alt[i, (k - 1) * F:k * F] = _top_excluding(zd[i, k - 1], tokens[i, k - 1], F)
             alt[i, (C - 1) * F] = int(np.argmax(zx[i]))
         out["alt_anchors"] = alt
+        out["z_next"] = zx  # the draft row of the position after the block (full-accept anchor)
     return out
 
 

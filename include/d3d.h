@@ -186,6 +186,29 @@ int branch_cache_match(const d3d_block_desc *descs, int total_blocks, const int3
                        const int32_t *n_accepted, const int32_t *next_token, int32_t *hit_branch,
                        hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Drafter token selection ([D3D] 方法步骤详情 step 4, 前置知识: 异步起草与缓存命中): the k best
+ * tokens of each logit row other than an excluded one. Order: larger logit first, ties to the lower
+ * token id; NaN logits count as -inf. Uses: the greedy drafted token of every masked position of the
+ * packed blocks (k = 1: argmax); the F alternative anchors of rejection position k = 1..C-1, i.e. the
+ * F best tokens of draft row k-1 other than the rejected draft token d_k (its residual mass is zero,
+ * so it can never be the replacement; k = F, exclude = d_k); the full-accept anchor (k = 1 over the
+ * row after the block).
+ *
+ *  logits   [rows_in, vocab] (dtype), DEVICE; vocab >= 1
+ *  rows     [n_rows] DEVICE row indexes into logits, or NULL for rows 0..n_rows-1
+ *  exclude  [n_rows] DEVICE token to skip per row (any value outside [0, vocab): none), or NULL
+ *  k        1..8; out DEVICE int32: row r's k tokens at out[out_off[r] .. + k-1] (out_off [n_rows]
+ *           DEVICE, or NULL for r * k); -1 where a row has fewer than k candidates
+ *  ws       at least draft_topk_workspace(n_rows, vocab, k) bytes; no initial contents required.
+ * Errors: D3D_EINVAL on bad sizes (n_rows < 1, vocab < 1, k outside 1..8) or NULL pointers;
+ * D3D_EWORKSPACE if ws is too small. Row indexes and offsets are not range-checked.
+ * ------------------------------------------------------------------------------------------- */
+size_t draft_topk_workspace(int n_rows, int vocab, int k);
+int draft_topk(d3d_dtype dtype, const void *logits, int vocab, int n_rows, const int32_t *rows,
+               const int32_t *exclude, int k, int32_t *out, const int32_t *out_off, void *ws,
+               size_t ws_bytes, hipStream_t stream);
+
 const char *d3d_status_string(int status);
 
 #ifdef __cplusplus

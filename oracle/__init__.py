@@ -15,6 +15,8 @@ NumPy from the pages (no blocking, fusion or reordering beyond the definition):
 * ``verify``    -- speculative-sampling verification: acceptance ratios, first rejection,
                    residual / bonus sampling, prefix-survival products and the acceptance length.
 * ``match``     -- the branch-cache hit test of the verified outcome against the drafted branches.
+* ``select``    -- drafter token selection: greedy drafted tokens and the alternative anchors of
+                   the branches (the k best tokens of a logit row other than an excluded one).
 
 Pages cited in this package:
 
@@ -26,4 +28,4 @@ Pages cited in this package:
 * [D3D-abs] the arXiv listing page of D3D (its English abstract).
 """
 
-from . import philox, packing, attention, verify, match  # noqa: F401
+from . import philox, packing, attention, verify, match, select  # noqa: F401

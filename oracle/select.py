@@ -1,0 +1,43 @@
+"""Drafter token selection (oracle side).
+
+[D3D, 方法步骤详情 step 4]: while the target verifies the current block, one packed drafter forward
+drafts continuation blocks for each of the first C-1 rejection positions with F alternative
+anchors each, plus a full-accept block. [D3D, 前置知识: 异步起草与缓存命中]: a branch is reused
+when the verified prefix starts like it. The pages do not say how the anchors or the drafted tokens
+are chosen; the readings (listed in the design doc, R3 and R17):
+
+* The drafted token of a masked position is the most likely token of its logits (greedy drafting,
+  the pages' own evaluation setting).
+* The F anchors of rejection position k (1-based; rejecting draft d_k) are the F most likely tokens
+  of the draft distribution Q_{k-1} (0-based row k-1, the row that judges d_k) other than d_k: a
+  rejection replaces d_k by a draw from max(0, P - Q), which is zero at d_k, so d_k can never be the
+  replacement. The full-accept anchor is the most likely token of the position after the block.
+* Order: larger logit first, ties to the lower token id (softmax at any temperature is monotone in
+  the logit, so this is the order of the probabilities). NaN logits count as -inf.
+
+TEST INFRASTRUCTURE: see the package docstring.
+"""
+
+import numpy as np
+
+
+def topk(row, k, exclude=-1):
+    """The k best tokens of one logit row other than `exclude`, larger logit first, ties to the lower
+    id; -1 pads the result when the row has fewer than k candidates."""
+    z = np.asarray(row, dtype=np.float64)
+    z = np.where(np.isnan(z), -np.inf, z)
+    order = np.lexsort((np.arange(z.size), -z))  # primary key -z (descending logit), then the id
+    order = order[order != exclude][:k]
+    out = np.full(k, -1, dtype=np.int64)
+    out[:order.size] = order
+    return out
+
+
+def alt_anchors(z_draft, tokens, z_next, coverage, fanout):
+    """Anchors of one request's branches in pack order: F per rejection position k = 1..C-1 (from
+    draft row k-1, excluding d_k = tokens[k-1]), then the full-accept anchor (from z_next)."""
+    out = []
+    for k in range(1, coverage):
+        out.extend(int(t) for t in topk(z_draft[k - 1], fanout, exclude=int(tokens[k - 1])))
+    out.append(int(topk(z_next, 1)[0]))
+    return np.array(out, dtype=np.int64)

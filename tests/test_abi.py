@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "draft_attn_packed", "draft_attn_packed_workspace",
-                 "spec_verify", "spec_verify_workspace", "branch_cache_match", "d3d_status_string"):
+                 "spec_verify", "spec_verify_workspace", "branch_cache_match", "draft_topk", "draft_topk_workspace",
+                 "d3d_status_string"):
         assert want in names
 
 
@@ -125,3 +126,14 @@ def test_workspace_sizes():
     assert _binding.draft_attn_packed_workspace("bf16", [0, 24], [4096], 16, 32, 8, 96) == 0
     assert _binding.spec_verify_workspace(16, 15, 151936) > 0
     assert _binding.spec_verify_workspace(1, 64, 10) == 0
+
+
+def test_topk_workspace():
+    # rows x chunks x k candidates of 8 bytes, 256-byte aligned; chunks fill one round of 2048 workgroups
+    # (at most 32 per row, at least 1024 tokens each)
+    assert _binding.draft_topk_workspace(384, 151936, 1) == 384 * 5 * 8
+    assert _binding.draft_topk_workspace(11, 151936, 2) % 256 == 0
+    assert _binding.draft_topk_workspace(11, 151936, 2) >= 11 * 32 * 2 * 8
+    assert _binding.draft_topk_workspace(1, 7, 8) == 256
+    for bad in ((0, 10, 1), (1, 0, 1), (1, 10, 0), (1, 10, 9)):
+        assert _binding.draft_topk_workspace(*bad) == 0
