@@ -412,11 +412,54 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},
     }
-    out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us)}
+    out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
+                        "kv_commit": next_row_commit(r, torch, mean_us)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def next_row_commit(r, torch, mean_us):
+    """KV commit (the second next row, not part of the step): each request's accepted slice (n_acc + 1
+    rows of block 0, n_acc from this round's verify outputs) appended to a paged cache at the end of
+    its prefix, plus promotion of the hit branch. The page table maps the pages around each prefix
+    end to a small pool (timing only); the prefix lengths are restored inside the graph before
+    each commit. Bytes = sum (n_acc + 1) x H_kv x d x 2 B x 2 (keys, values) x 2 (read, write)."""
+    B, n_req = r.B, r.n_req
+    hkv, d = int(r.k_new.shape[1]), int(r.k_new.shape[2])
+    ps = 16
+    lens0 = torch.tensor(r.lens_i32, dtype=torch.int32, device="cuda")
+    span = (B + ps - 1) // ps + 1  # pages a slice of at most B tokens can touch
+    max_pages = max(r.lens) // ps + span
+    table = torch.full((n_req, max_pages), -1, dtype=torch.int32)
+    for i, L in enumerate(r.lens):
+        for p in range(span):
+            table[i, L // ps + p] = span * i + p
+    table = table.cuda()
+    kc = torch.zeros((span * n_req, ps, hkv, d), dtype=r.k_new.dtype, device="cuda")
+    vc = torch.zeros_like(kc)
+    lens = lens0.clone()
+    tokens = torch.zeros(int(r.q.shape[0]), dtype=torch.int32, device="cuda")
+    nxt = torch.empty((n_req, B), dtype=torch.int32, device="cuda")
+    status = torch.empty(n_req, dtype=torch.int32, device="cuda")
+    n_acc = r.ver_out["n_accepted"]
+
+    def fn():
+        lens.copy_(lens0)
+        r.lib.kv_commit(r.k_new, r.v_new, kc, vc, table, r.off_dev, lens, n_acc, B, hit=r.hit, packed_tokens=tokens,
+                        next_block=nxt, status=status)
+
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    t = mean_us(g, 100)
+    rows = int((n_acc.clamp(0, B - 1) + 1).sum().item())
+    nbytes = rows * hkv * d * r.k_new.element_size() * 2 * 2
+    return {"rows": rows, "us": round(t, 3), "gbs": round(nbytes / (t * 1e-6) / 1e9, 2),
+            "note": "graph also restores the prefix lengths (one small device copy)"}
 
 
 def next_row_topk(r, torch, cur, mean_us):

@@ -44,6 +44,9 @@ _SIGNATURES = {
     "draft_topk_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
     "draft_topk": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int,
                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "kv_commit": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
+                             _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
+                             _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "d3d_status_string": (_c.c_char_p, [_c.c_int]),
 }
 EXPORTS = tuple(_SIGNATURES)
@@ -306,3 +309,44 @@ def draft_topk(logits, k, rows=None, exclude=None, out=None, out_off=None, n_row
                            _ptr(ws), need, _stream(stream))
     _check(st, "draft_topk")
     return out
+
+
+def kv_commit(k_new, v_new, k_cache, v_cache, page_table, req_block_off, prefix_len, n_accepted, block_size,
+              hit=None, packed_tokens=None, next_block=None, status=None, stream=None):
+    """Append each request's accepted slice to the paged cache (prefix_len updated in place) and, with
+    hit / packed_tokens, promote the hit branch. k_new / v_new [N_q, H_kv, d]; caches [pages, page, H_kv,
+    d]; page_table [n_req, max_pages]; req_block_off [n_req + 1]; prefix_len, n_accepted, hit [n_req];
+    packed_tokens [N_q]; all int32 / GPU. Returns (next_block or None, status)."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (page_table, "page_table"), (req_block_off, "req_block_off"), (prefix_len, "prefix_len"),
+                 (n_accepted, "n_accepted")):
+        _dev(t, n)
+    dt = _dtype_code(k_new)
+    if not (k_new.dtype == v_new.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("k_new, v_new and the caches must share a dtype")
+    hkv, d = k_new.shape[1], k_new.shape[2]
+    if k_cache.shape != v_cache.shape or k_cache.shape[2:] != (hkv, d):
+        raise ValueError("caches must be [pages, page_size, H_kv, d] like k_new's rows")
+    n_req = n_accepted.numel()
+    for t, n in ((page_table, "page_table"), (req_block_off, "req_block_off"), (prefix_len, "prefix_len"),
+                 (n_accepted, "n_accepted")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    if page_table.dim() != 2 or page_table.shape[0] != n_req or req_block_off.numel() != n_req + 1 \
+            or prefix_len.numel() != n_req:
+        raise ValueError("page_table / req_block_off / prefix_len do not match n_accepted")
+    if (hit is None) != (packed_tokens is None):
+        raise ValueError("pass hit and packed_tokens together")
+    if hit is not None:
+        _dev(hit, "hit")
+        _dev(packed_tokens, "packed_tokens")
+        if next_block is None:
+            next_block = torch.empty((n_req, block_size), dtype=torch.int32, device=k_new.device)
+    if status is None:
+        status = torch.empty(n_req, dtype=torch.int32, device=k_new.device)
+    st = load().kv_commit(dt, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                          k_cache.shape[1], page_table.shape[1], k_cache.shape[0], _ptr(req_block_off),
+                          _ptr(prefix_len), _ptr(n_accepted), n_req, block_size, hkv, d, _ptr(hit),
+                          _ptr(packed_tokens), _ptr(next_block), _ptr(status), _stream(stream))
+    _check(st, "kv_commit")
+    return next_block, status

@@ -209,6 +209,33 @@ int draft_topk(d3d_dtype dtype, const void *logits, int vocab, int n_rows, const
                const int32_t *exclude, int k, int32_t *out, const int32_t *out_off, void *ws,
                size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * KV commit of the accepted slice and promotion of the hit branch ([D3D] 前置知识: 异步起草与缓存命中,
+ * 方法步骤详情 step 4). After verification request i's prefix grows by its anchor and accepted drafts:
+ * rows 0..n_acc_i of its block 0 in the packed k_new / v_new (causal in-block, so they are prefix
+ * keys / values) are copied to the paged cache at token positions prefix_len[i] .. + n_acc_i, and
+ * prefix_len[i] grows by n_acc_i + 1. With hit / packed_tokens / next_block given, next_block[i]
+ * receives the B packed tokens of the hit branch (block hit_i of request i; the next round's current
+ * block), or B times -1 on a miss.
+ *
+ *  k_new, v_new   [N_q, H_kv, d] (dtype), DEVICE, 16-byte aligned; the packed rows of the round
+ *  k_cache, v_cache [num_pages, page_size, H_kv, d], DEVICE, 16-byte aligned
+ *  page_table     [n_req, max_pages] int32 DEVICE
+ *  req_block_off  [n_req + 1] int32 DEVICE (packed block offsets); prefix_len [n_req] int32 DEVICE,
+ *                 read and updated; n_accepted [n_req] int32 DEVICE (clamped to [0, B-1])
+ *  hit [n_req], packed_tokens [N_q], next_block [n_req, B] int32 DEVICE, all NULL or all given
+ *  status [n_req] int32 DEVICE or NULL: 0 = committed; 1 = a slice row had no cache slot (page index
+ *         past max_pages or page id outside [0, num_pages)): rows with a slot are still copied, and
+ *         prefix_len grows only by the rows before the first row without one.
+ * 1 <= B <= 256; H_kv * d * element size a multiple of 16. Errors: D3D_EINVAL on bad sizes or NULL
+ * required pointers, D3D_EUNSUPPORTED on a row size that is not a multiple of 16 bytes.
+ * ------------------------------------------------------------------------------------------- */
+int kv_commit(d3d_dtype dtype, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+              const int32_t *page_table, int page_size, int max_pages, int num_pages,
+              const int32_t *req_block_off, int32_t *prefix_len, const int32_t *n_accepted, int n_req,
+              int block_size, int n_heads_kv, int head_dim, const int32_t *hit,
+              const int32_t *packed_tokens, int32_t *next_block, int32_t *status, hipStream_t stream);
+
 const char *d3d_status_string(int status);
 
 #ifdef __cplusplus

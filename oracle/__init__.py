@@ -17,6 +17,8 @@ NumPy from the pages (no blocking, fusion or reordering beyond the definition):
 * ``match``     -- the branch-cache hit test of the verified outcome against the drafted branches.
 * ``select``    -- drafter token selection: greedy drafted tokens and the alternative anchors of
                    the branches (the k best tokens of a logit row other than an excluded one).
+* ``commit``    -- the accepted slice appended to the paged drafter cache, and the hit branch
+                   promoted to the next round's current block.
 
 Pages cited in this package:
 
@@ -28,4 +30,4 @@ Pages cited in this package:
 * [D3D-abs] the arXiv listing page of D3D (its English abstract).
 """
 
-from . import philox, packing, attention, verify, match, select  # noqa: F401
+from . import philox, packing, attention, verify, match, select, commit  # noqa: F401
