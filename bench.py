@@ -413,11 +413,47 @@ def main():
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},
     }
     out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
-                        "kv_commit": next_row_commit(r, torch, mean_us)}
+                        "kv_commit": next_row_commit(r, torch, mean_us),
+                        "awl_loss": next_row_awl(r, torch, mean_us)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def next_row_awl(r, torch, mean_us, n_blocks=128, n_pos=15):
+    """Acceptance-weighted drafter-training loss with its gradient (the fourth next row, not part of
+    the step) at one training sample's shape: 128 anchor blocks x 15 future positions (B = 16) over
+    the workload's vocabulary. Logits, tokens, labels and the inclusion mask are drawn on the device
+    (timing only; the tests check this shape against the oracle). HBM bytes = rows x V x 2 B x 4:
+    target and draft logits read for the statistics, the draft logits read again and the gradient
+    written."""
+    w, lib = r.w, r.lib
+    if w.dtype != "bf16":
+        return None
+    V = w.vocab
+    gen = torch.Generator(device="cuda").manual_seed(w.seed + 4)
+    zt = (torch.randn((n_blocks, n_pos, V), generator=gen, device="cuda") * 2.0).to(torch.bfloat16)
+    zd = (zt.float() + torch.randn((n_blocks, n_pos, V), generator=gen, device="cuda")).to(torch.bfloat16)
+    tok = zd.argmax(dim=-1).to(torch.int32)
+    lab = zt.argmax(dim=-1).to(torch.int32)
+    inc = (torch.rand((n_blocks, n_pos), generator=gen, device="cuda") < 0.85).to(torch.int32)
+    out = lib.awl_loss(zt, zd, tok, lab, include=inc, grad=True)
+    ws = torch.empty(lib.awl_loss_workspace(n_blocks, n_pos, V), dtype=torch.uint8, device="cuda")
+
+    def fn():
+        lib.awl_loss(zt, zd, tok, lab, include=inc, grad=True, out=out, ws=ws)
+
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    t = mean_us(g, 50)
+    nbytes = n_blocks * n_pos * V * 2 * 4
+    gbs = nbytes / (t * 1e-6) / 1e9
+    return {"shape": [n_blocks, n_pos, V], "us": round(t, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
 def next_row_commit(r, torch, mean_us):

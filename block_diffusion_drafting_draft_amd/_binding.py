@@ -47,6 +47,10 @@ _SIGNATURES = {
     "kv_commit": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
                              _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
                              _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "awl_loss_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
+    "awl_loss": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
+                            _c.c_int, _c.c_int, _c.c_double, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                            _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "d3d_status_string": (_c.c_char_p, [_c.c_int]),
 }
 EXPORTS = tuple(_SIGNATURES)
@@ -350,3 +354,44 @@ def kv_commit(k_new, v_new, k_cache, v_cache, page_table, req_block_off, prefix_
                           _ptr(packed_tokens), _ptr(next_block), _ptr(status), _stream(stream))
     _check(st, "kv_commit")
     return next_block, status
+
+
+def awl_loss_workspace(n_blocks, n_pos, vocab):
+    return int(load().awl_loss_workspace(n_blocks, n_pos, vocab))
+
+
+def awl_loss(target_logits, draft_logits, draft_tokens, labels, include=None, eps=1e-6, grad=False, out=None,
+             ws=None, stream=None):
+    """Acceptance-weighted loss. target / draft logits [n_blocks, n_pos, V]; draft_tokens, labels,
+    include int32 [n_blocks, n_pos] (include None: all), all on the GPU. Returns a dict of device
+    tensors: loss (float64 [1]), weights, ce (float32 [n_blocks, n_pos]) and grad (like draft_logits)
+    when grad=True."""
+    for t, n in ((target_logits, "target_logits"), (draft_logits, "draft_logits"), (draft_tokens, "draft_tokens"),
+                 (labels, "labels")):
+        _dev(t, n)
+    dt = _dtype_code(draft_logits)
+    if target_logits.dtype != draft_logits.dtype or target_logits.shape != draft_logits.shape:
+        raise ValueError("target and draft logits must share dtype and shape")
+    n_blocks, n_pos, vocab = draft_logits.shape
+    for t, n in ((draft_tokens, "draft_tokens"), (labels, "labels"), (include, "include")):
+        if t is not None:
+            _dev(t, n)
+            if t.dtype != torch.int32 or t.shape != (n_blocks, n_pos):
+                raise ValueError(f"{n} must be int32 [n_blocks, n_pos]")
+    dev = draft_logits.device
+    if out is None:
+        out = dict(loss=torch.empty(1, dtype=torch.float64, device=dev),
+                   weights=torch.empty((n_blocks, n_pos), dtype=torch.float32, device=dev),
+                   ce=torch.empty((n_blocks, n_pos), dtype=torch.float32, device=dev))
+        if grad:
+            out["grad"] = torch.empty_like(draft_logits)
+    need = awl_loss_workspace(n_blocks, n_pos, vocab)
+    if need == 0:
+        raise ValueError("unsupported awl_loss shape")
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = load().awl_loss(dt, _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(labels), _ptr(include),
+                         n_blocks, n_pos, vocab, float(eps), _ptr(out["weights"]), _ptr(out.get("ce")),
+                         _ptr(out["loss"]), _ptr(out.get("grad")), _ptr(ws), need, _stream(stream))
+    _check(st, "awl_loss")
+    return out

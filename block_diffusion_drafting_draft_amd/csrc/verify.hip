@@ -89,36 +89,6 @@ struct VerifyArgs {
   double *mass_part;  // [n_req][s_chunks]
 };
 
-// exp(x) in fp64 for x < 709 (the arguments here are differences from a row reference, at most
-// about 84, or log-probabilities). Cody-Waite argument reduction (W. J. Cody and W. Waite, "Software
-// Manual for the Elementary Functions", 1980): x = k ln2 + r with |r| <= ln2/2, ln2 split into a
-// 21-bit head (k * head is exact) and a tail; then the Taylor series of e^r to degree 12
-// (truncation below 2e-16 relative) and a scaling by 2^k. About 18 fp64 operations. NaN (from
-// -inf - -inf) and arguments below the smallest subnormal give 0.
-__device__ __forceinline__ double exp_fp64(double x) {
-  constexpr double kInvLn2 = 1.4426950408889634;
-  constexpr double kLn2Hi = 0.6931467056274414;      // ln 2 with its low 32 mantissa bits cleared
-  constexpr double kLn2Lo = 4.7493250390316726e-07;  // ln 2 - kLn2Hi
-  if (!(x > -745.5)) return 0.0;
-  const double k = rint(x * kInvLn2);
-  double r = fma(-k, kLn2Hi, x);
-  r = fma(-k, kLn2Lo, r);
-  double p = 2.08767569878681e-09;  // 1/12!
-  p = fma(p, r, 2.505210838544172e-08);
-  p = fma(p, r, 2.755731922398589e-07);
-  p = fma(p, r, 2.7557319223985893e-06);
-  p = fma(p, r, 2.48015873015873e-05);
-  p = fma(p, r, 0.0001984126984126984);
-  p = fma(p, r, 0.001388888888888889);
-  p = fma(p, r, 0.008333333333333333);
-  p = fma(p, r, 0.041666666666666664);
-  p = fma(p, r, 0.16666666666666666);
-  p = fma(p, r, 0.5);
-  p = fma(p, r, 1.0);
-  p = fma(p, r, 1.0);
-  return ldexp(p, static_cast<int>(k));
-}
-
 // ------------------------------------------------------------------------------------------------
 // block reductions (256 threads = 4 wavefronts)
 // ------------------------------------------------------------------------------------------------

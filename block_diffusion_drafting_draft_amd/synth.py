@@ -180,6 +180,38 @@ def verify_inputs(w, n_req=None, vocab=None, block_size=None, seed=None, tempera
 
 
 # --------------------------------------------------------------------------------------------
+# Drafter-training loss inputs
+# --------------------------------------------------------------------------------------------
+
+def awl_inputs(n_blocks, n_pos, vocab, dtype="bf16", seed=0, sigma=2.0, noise=1.0, greedy=0.7, include=0.85):
+    """Logits and labels of one training step's diffusion blocks (n_pos future positions each).
+
+    Target logits are iid N(0, sigma); the draft's are the target's plus N(0, noise), so the two
+    distributions agree only roughly. Draft tokens are the draft's most likely token with probability
+    `greedy`, else uniform; labels are the target's most likely token with probability `greedy`, else
+    uniform; each position is in the loss with probability `include`. Rows are drawn in slices so
+    that no float64 copy of the whole batch is made. Returns float32 (bf16-exact for bf16) arrays
+    z_target, z_draft [n_blocks, n_pos, V] and int32 tokens, labels, include [n_blocks, n_pos]."""
+    rng = np.random.default_rng([seed, 23])
+    rows = n_blocks * n_pos
+    zt = np.empty((rows, vocab), dtype=np.float32)
+    zd = np.empty((rows, vocab), dtype=np.float32)
+    step = max(1, (1 << 24) // max(vocab, 1))
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        t = rng.standard_normal((r1 - r0, vocab), dtype=np.float32) * np.float32(sigma)
+        d = t + rng.standard_normal((r1 - r0, vocab), dtype=np.float32) * np.float32(noise)
+        zt[r0:r1] = _cast(t, dtype)
+        zd[r0:r1] = _cast(d, dtype)
+    pick = lambda z: np.where(rng.random(rows) < greedy, np.argmax(z, axis=1), rng.integers(0, vocab, size=rows))
+    tokens = pick(zd).astype(np.int32).reshape(n_blocks, n_pos)
+    labels = pick(zt).astype(np.int32).reshape(n_blocks, n_pos)
+    inc = (rng.random(rows) < include).astype(np.int32).reshape(n_blocks, n_pos)
+    return dict(z_target=zt.reshape(n_blocks, n_pos, vocab), z_draft=zd.reshape(n_blocks, n_pos, vocab),
+                tokens=tokens, labels=labels, include=inc)
+
+
+# --------------------------------------------------------------------------------------------
 # Attention inputs
 # --------------------------------------------------------------------------------------------
 

@@ -236,6 +236,30 @@ int kv_commit(d3d_dtype dtype, const void *k_new, const void *v_new, void *k_cac
               int block_size, int n_heads_kv, int head_dim, const int32_t *hit,
               const int32_t *packed_tokens, int32_t *next_block, int32_t *status, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Acceptance-weighted loss of drafter training ([DScout] 前置知识: 接受加权损失 AWL 与推测采样接受规则;
+ * 方法步骤详情 step 4). For block r and future position k (0..n_pos-1), with P / Q the softmaxes of
+ * the target / draft logits (temperature 1) and y the draft token:
+ *   alpha_{r,k} = min(1, P(y) / Q(y))  (1 when Q(y) = 0);  w_{r,k} = prod_{j<k} alpha_{r,j}, w_{r,0} = 1
+ *   L = sum I w CE / (sum I w + eps),  CE = -log Q(y*)
+ * and, when grad is given, dL/dz^Q = I w / (sum I w + eps) * (Q - onehot(y*)) (w is a stop-gradient;
+ * the target receives no gradient). Precision as in spec_verify: fp32 exp per element, fp64
+ * accumulation, fp64 scalars; the gradient is computed in fp32 and stored in the logits' dtype.
+ *
+ *  target_logits, draft_logits [n_blocks, n_pos, vocab] (dtype) DEVICE; 1 <= n_pos <= 63
+ *  draft_tokens, labels [n_blocks, n_pos] int32 DEVICE (clamped to [0, vocab)); include the same
+ *  shape int32 DEVICE (0 = not in the loss) or NULL (all); eps >= 0 (the pages use 1e-6)
+ *  outputs DEVICE: weights [n_blocks, n_pos] f32, ce the same or NULL, loss one double,
+ *  grad [n_blocks, n_pos, vocab] (dtype) or NULL
+ *  ws: at least awl_loss_workspace(n_blocks, n_pos, vocab) bytes; no initial contents required.
+ * Errors: D3D_EINVAL on bad sizes, eps or NULL required pointers; D3D_EWORKSPACE.
+ * ------------------------------------------------------------------------------------------- */
+size_t awl_loss_workspace(int n_blocks, int n_pos, int vocab);
+int awl_loss(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+             const int32_t *draft_tokens, const int32_t *labels, const int32_t *include, int n_blocks,
+             int n_pos, int vocab, double eps, float *weights, float *ce, double *loss, void *grad,
+             void *ws, size_t ws_bytes, hipStream_t stream);
+
 const char *d3d_status_string(int status);
 
 #ifdef __cplusplus

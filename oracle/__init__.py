@@ -19,6 +19,7 @@ NumPy from the pages (no blocking, fusion or reordering beyond the definition):
                    the branches (the k best tokens of a logit row other than an excluded one).
 * ``commit``    -- the accepted slice appended to the paged drafter cache, and the hit branch
                    promoted to the next round's current block.
+* ``awl``       -- the acceptance-weighted training loss of the drafter and its gradient.
 
 Pages cited in this package:
 
@@ -30,4 +31,4 @@ Pages cited in this package:
 * [D3D-abs] the arXiv listing page of D3D (its English abstract).
 """
 
-from . import philox, packing, attention, verify, match, select, commit  # noqa: F401
+from . import philox, packing, attention, verify, match, select, commit, awl  # noqa: F401
