@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match"), default=None,
+    p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss"),
+                   default=None,
                    help="only replay this call's graph (warmup + steps times, nothing else on the GPU) and print "
                         "its event-timed duration: the command to profile one call's kernels alone")
     return p.parse_args()
@@ -263,7 +264,7 @@ def main():
     torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
     if args.call:
-        g = graphs[args.call]
+        g = awl_graph(r, torch)[0] if args.call == "awl_loss" else graphs[args.call]
         for _ in range(args.warmup):
             g.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -421,13 +422,13 @@ def main():
     return 0
 
 
-def next_row_awl(r, torch, mean_us, n_blocks=128, n_pos=15):
-    """Acceptance-weighted drafter-training loss with its gradient (the fourth next row, not part of
-    the step) at one training sample's shape: 128 anchor blocks x 15 future positions (B = 16) over
-    the workload's vocabulary. Logits, tokens, labels and the inclusion mask are drawn on the device
-    (timing only; the tests check this shape against the oracle). HBM bytes = rows x V x 2 B x 4:
-    target and draft logits read for the statistics, the draft logits read again and the gradient
-    written."""
+def awl_graph(r, torch, n_blocks=128, n_pos=15):
+    """Graph of one awl_loss call with its gradient at one training sample's shape: 128 anchor blocks
+    x 15 future positions (B = 16) over the workload's vocabulary. Logits, tokens, labels and the
+    inclusion mask are drawn on the device (timing only; the tests check this shape against the
+    oracle). HBM bytes = rows x V x 2 B x 4: target and draft logits read for the statistics, the
+    draft logits read again and the gradient written. Returns (graph, bytes, shape), or None when the
+    workload's logits are not bf16."""
     w, lib = r.w, r.lib
     if w.dtype != "bf16":
         return None
@@ -449,10 +450,20 @@ def next_row_awl(r, torch, mean_us, n_blocks=128, n_pos=15):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
+    g.keep = (zt, zd, tok, lab, inc, out, ws)
+    return g, n_blocks * n_pos * V * 2 * 4, [n_blocks, n_pos, V]
+
+
+def next_row_awl(r, torch, mean_us):
+    """Acceptance-weighted drafter-training loss with its gradient (the fourth next row, not part of
+    the step), timed as the mean of back-to-back graph replays."""
+    made = awl_graph(r, torch)
+    if made is None:
+        return None
+    g, nbytes, shape = made
     t = mean_us(g, 50)
-    nbytes = n_blocks * n_pos * V * 2 * 4
     gbs = nbytes / (t * 1e-6) / 1e9
-    return {"shape": [n_blocks, n_pos, V], "us": round(t, 3), "bytes": nbytes, "gbs": round(gbs, 1),
+    return {"shape": shape, "us": round(t, 3), "bytes": nbytes, "gbs": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 

@@ -20,6 +20,13 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies; workgroups roun
 // bf16 <-> f32 (bf16 is the upper half of an IEEE binary32 value).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// two fp32 values rounded to nearest-even bf16, packed low / high
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
 __device__ __forceinline__ float load_elem(const __bf16 *p) {
   return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t *>(p)) << 16);
 }
