@@ -20,6 +20,8 @@ NumPy from the pages (no blocking, fusion or reordering beyond the definition):
 * ``commit``    -- the accepted slice appended to the paged drafter cache, and the hit branch
                    promoted to the next round's current block.
 * ``awl``       -- the acceptance-weighted training loss of the drafter and its gradient.
+* ``train_attn`` -- training-time packed attention (response causal, blocks on their anchor's
+                   prefix, bidirectional inside a block), forward and backward.
 
 Pages cited in this package:
 
@@ -31,4 +33,4 @@ Pages cited in this package:
 * [D3D-abs] the arXiv listing page of D3D (its English abstract).
 """
 
-from . import philox, packing, attention, verify, match, select, commit, awl  # noqa: F401
+from . import philox, packing, attention, verify, match, select, commit, awl, train_attn  # noqa: F401

@@ -1,0 +1,93 @@
+"""Training-time packed attention, forward and backward (oracle side).
+
+[D3D, 方法步骤详情 step 2] and [D3D, 核心方法]: anchors are drawn in each training response; every
+anchor starts a diffusion block of B tokens (the anchor itself visible, the B-1 positions after it
+masked); all blocks are packed into one sequence after the response; the response is encoded
+causally once and shared as the prefix of every block, and attention inside a block is
+bidirectional. The clean response rows are computed too (they carry the autoregressive loss).
+[DScout, 方法步骤详情 step 2]: the horizon B is drawn per update from {8, 16, 24, 32}.
+
+Reading (listed in the design doc, R20): packed rows 0..L-1 are the response; block i occupies rows
+L + i*B .. L + i*B + B - 1 and its anchor sits at response position a_i. A response row p sees the
+response keys j <= p. A row of block i sees the response keys j < a_i (the tokens before its anchor)
+and every row of block i. No row sees another block.
+
+Forward, per query head h with key/value head g(h) = h // (H_q / H_kv):
+    s = scale * q k^T (masked to -inf),  lse = log sum_j exp(s),  o = exp(s - lse) v.
+Backward of a scalar loss with upstream gradient do: with P = exp(s - lse) and D_r = sum_d do_r o_r,
+    dS = P * (do v^T - D),  dq = scale dS k,  dk = scale dS^T q,  dv = P^T do,
+dk and dv summed over the query heads of a group. Everything in float64 on the exact input values.
+
+TEST INFRASTRUCTURE: see the package docstring.
+"""
+
+import numpy as np
+
+
+def n_rows(L, n_blocks, B):
+    return L + n_blocks * B
+
+
+def visible_mask(L, anchors, B):
+    """bool [N, N]: mask[r, j] is True when packed row r sees packed key j (the reading above)."""
+    anchors = [int(a) for a in anchors]
+    n = n_rows(L, len(anchors), B)
+    mask = np.zeros((n, n), dtype=bool)
+    for p in range(L):
+        mask[p, :p + 1] = True
+    for i, a in enumerate(anchors):
+        r0 = L + i * B
+        mask[r0:r0 + B, :a] = True
+        mask[r0:r0 + B, r0:r0 + B] = True
+    return mask
+
+
+def _group(hq, hkv):
+    if hq % hkv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    return hq // hkv
+
+
+def forward(q, k, v, L, anchors, B, scale):
+    """q [N, H_q, d], k, v [N, H_kv, d] -> (o float64 [N, H_q, d], lse float64 [N, H_q])."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    n, hq, d = q.shape
+    grp = _group(hq, k.shape[1])
+    mask = visible_mask(L, anchors, B)
+    if mask.shape[0] != n:
+        raise ValueError("row count does not match L + n_blocks * B")
+    o = np.empty_like(q)
+    lse = np.empty((n, hq))
+    for h in range(hq):
+        g = h // grp
+        s = np.where(mask, (q[:, h] @ k[:, g].T) * float(scale), -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        tot = e.sum(axis=1, keepdims=True)
+        lse[:, h] = (m + np.log(tot))[:, 0]
+        o[:, h] = (e / tot) @ v[:, g]
+    return o, lse
+
+
+def backward(q, k, v, do, L, anchors, B, scale):
+    """Gradients (dq [N, H_q, d], dk, dv [N, H_kv, d]) of sum(o * do), float64."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    n, hq, d = q.shape
+    hkv = k.shape[1]
+    grp = _group(hq, hkv)
+    mask = visible_mask(L, anchors, B)
+    o, lse = forward(q, k, v, L, anchors, B, scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        g = h // grp
+        s = np.where(mask, (q[:, h] @ k[:, g].T) * float(scale), -np.inf)
+        p = np.exp(s - lse[:, h:h + 1])
+        dp = do[:, h] @ v[:, g].T
+        dd = np.sum(do[:, h] * o[:, h], axis=1, keepdims=True)
+        ds = p * (dp - dd)
+        dq[:, h] = float(scale) * (ds @ k[:, g])
+        dk[:, g] += float(scale) * (ds.T @ q[:, h])
+        dv[:, g] += p.T @ do[:, h]
+    return dq, dk, dv
