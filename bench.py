@@ -47,7 +47,8 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss"),
+    p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss",
+                                     "train_attn_fwd", "train_attn_bwd"),
                    default=None,
                    help="only replay this call's graph (warmup + steps times, nothing else on the GPU) and print "
                         "its event-timed duration: the command to profile one call's kernels alone")
@@ -264,7 +265,12 @@ def main():
     torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
     if args.call:
-        g = awl_graph(r, torch)[0] if args.call == "awl_loss" else graphs[args.call]
+        if args.call == "awl_loss":
+            g = awl_graph(r, torch)[0]
+        elif args.call in ("train_attn_fwd", "train_attn_bwd"):
+            g = train_attn_graphs(r, torch)[0 if args.call == "train_attn_fwd" else 1]
+        else:
+            g = graphs[args.call]
         for _ in range(args.warmup):
             g.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -415,7 +421,8 @@ def main():
     }
     out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
                         "kv_commit": next_row_commit(r, torch, mean_us),
-                        "awl_loss": next_row_awl(r, torch, mean_us)}
+                        "awl_loss": next_row_awl(r, torch, mean_us),
+                        "train_attn": next_row_train_attn(r, torch, mean_us)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
@@ -452,6 +459,53 @@ def awl_graph(r, torch, n_blocks=128, n_pos=15):
         fn()
     g.keep = (zt, zd, tok, lab, inc, out, ws)
     return g, n_blocks * n_pos * V * 2 * 4, [n_blocks, n_pos, V]
+
+
+def train_attn_graphs(r, torch, L=4096, n_blocks=128, B=16):
+    """Graphs of the training-time packed attention forward and backward at one training sample's
+    shape: a 4096-token response with 128 anchors (sorted, drawn uniformly), B = 16, the drafter's
+    32 query / 8 key-value heads of dimension 128. q, k, v, dout are N(0, 1) bf16 drawn on the device
+    (timing only; the tests check this shape against the oracle). Returns (fwd graph, bwd graph,
+    visible (row, key) pairs per query head)."""
+    gen = torch.Generator(device="cuda").manual_seed(r.w.seed + 5)
+    hq, hkv, d = 32, 8, 128
+    N = L + n_blocks * B
+    q = torch.randn((N, hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((N, hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((N, hkv, d), generator=gen, device="cuda").to(torch.bfloat16)
+    dout = torch.randn((N, hq, d), generator=gen, device="cuda").to(torch.bfloat16)
+    anchors = torch.sort(torch.randint(0, L + 1, (n_blocks,), generator=gen, device="cuda"))[0].to(torch.int32)
+    lib = r.lib
+    out, lse = lib.train_attn_fwd(q, k, v, anchors, L, B)
+    dq, dk, dv = lib.train_attn_bwd(q, k, v, out, dout, lse, anchors, L, B)
+    ws = torch.empty(lib.train_attn_workspace(L, n_blocks, B, hq, hkv), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    gf, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf):
+        lib.train_attn_fwd(q, k, v, anchors, L, B, out=out, lse=lse)
+    with torch.cuda.graph(gb):
+        lib.train_attn_bwd(q, k, v, out, dout, lse, anchors, L, B, dq=dq, dk=dk, dv=dv, ws=ws)
+    keep = (q, k, v, dout, anchors, out, lse, dq, dk, dv, ws)
+    gf.keep = gb.keep = keep
+    a = anchors.cpu().numpy().astype(np.int64)
+    pairs = L * (L + 1) // 2 + int(np.sum(B * (a + B)))
+    return gf, gb, pairs * hq
+
+
+def next_row_train_attn(r, torch, mean_us):
+    """Training-time packed attention (the third next row): forward and backward, each the mean of
+    back-to-back graph replays. Algorithmic FLOPs per visible (row, key) pair and query head: 4 d
+    forward (q.k and p.v), 10 d backward (s recomputed, dP, dV, dK, dQ)."""
+    gf, gb, pairs = train_attn_graphs(r, torch)
+    d = 128
+    tf, tb = mean_us(gf, 20), mean_us(gb, 20)
+    ff, fb = 4 * d * pairs, 10 * d * pairs
+    peak = MFMA_BF16_PEAK_TFLOPS
+    return {"shape": "L 4096 + 128 x 16, 32/8 heads, d 128", "visible_pairs_per_head": pairs // 32,
+            "fwd_us": round(tf, 2), "bwd_us": round(tb, 2),
+            "fwd_tflops": round(ff / tf / 1e6, 1), "bwd_tflops": round(fb / tb / 1e6, 1),
+            "fwd_pct_mfma_peak": round(100 * ff / tf / 1e6 / peak, 2),
+            "bwd_pct_mfma_peak": round(100 * fb / tb / 1e6 / peak, 2)}
 
 
 def next_row_awl(r, torch, mean_us):
@@ -560,11 +614,8 @@ def next_row_topk(r, torch, cur, mean_us):
 
 
 def _kernel_digest():
-    import hashlib
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_diffusion_drafting_draft_amd", "csrc",
-                       "attn.hip")
-    with open(src, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    from block_diffusion_drafting_draft_amd import traffic
+    return traffic.source_digest()
 
 
 if __name__ == "__main__":

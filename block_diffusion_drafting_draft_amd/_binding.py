@@ -51,6 +51,10 @@ _SIGNATURES = {
     "awl_loss": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
                             _c.c_int, _c.c_int, _c.c_double, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                             _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "train_attn_workspace": (_c.c_size_t, [_c.c_int] * 5),
+    "train_attn_fwd": (_c.c_int, [_c.c_int] + [_c.c_void_p] * 4 + [_c.c_int] * 6 + [_c.c_float] + [_c.c_void_p] * 3),
+    "train_attn_bwd": (_c.c_int, [_c.c_int] + [_c.c_void_p] * 7 + [_c.c_int] * 6 + [_c.c_float] + [_c.c_void_p] * 4
+                       + [_c.c_size_t, _c.c_void_p]),
     "d3d_status_string": (_c.c_char_p, [_c.c_int]),
 }
 EXPORTS = tuple(_SIGNATURES)
@@ -395,3 +399,58 @@ def awl_loss(target_logits, draft_logits, draft_tokens, labels, include=None, ep
                          _ptr(out["loss"]), _ptr(out.get("grad")), _ptr(ws), need, _stream(stream))
     _check(st, "awl_loss")
     return out
+
+
+def _train_shape(q, k, anchors, L, block_size):
+    for t, n in ((q, "q"), (k, "k"), (anchors, "anchors")):
+        _dev(t, n)
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16:
+        raise TypeError("training attention takes bf16 tensors")
+    if anchors.dtype != torch.int32 or anchors.dim() != 1:
+        raise ValueError("anchors must be int32 [n_blocks]")
+    n_blocks = anchors.numel()
+    N, hq, d = q.shape
+    if N != L + n_blocks * block_size or k.shape[0] != N or k.shape[2] != d:
+        raise ValueError("q / k rows must be L + n_blocks * block_size")
+    return n_blocks, N, hq, k.shape[1], d
+
+
+def train_attn_workspace(L, n_blocks, block_size, n_heads_q, n_heads_kv):
+    return int(load().train_attn_workspace(L, n_blocks, block_size, n_heads_q, n_heads_kv))
+
+
+def train_attn_fwd(q, k, v, anchors, L, block_size, scale=None, out=None, lse=None, stream=None):
+    """Training-time packed attention forward. q [N, H_q, d], k, v [N, H_kv, d] bf16, anchors int32
+    [n_blocks] (all on the GPU). Returns (out [N, H_q, d] bf16, lse [N, H_q] f32)."""
+    n_blocks, N, hq, hkv, d = _train_shape(q, k, anchors, L, block_size)
+    _dev(v, "v")
+    scale = d ** -0.5 if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((N, hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = load().train_attn_fwd(D3D_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(anchors), L, n_blocks, block_size, hq, hkv, d,
+                               float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "train_attn_fwd")
+    return out, lse
+
+
+def train_attn_bwd(q, k, v, out, dout, lse, anchors, L, block_size, scale=None, dq=None, dk=None, dv=None, ws=None,
+                   stream=None):
+    """Training-time packed attention backward: (dq, dk, dv) from the forward's out, lse and the
+    upstream gradient dout (bf16 tensors on the GPU)."""
+    n_blocks, N, hq, hkv, d = _train_shape(q, k, anchors, L, block_size)
+    for t, n in ((v, "v"), (out, "out"), (dout, "dout"), (lse, "lse")):
+        _dev(t, n)
+    scale = d ** -0.5 if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = train_attn_workspace(L, n_blocks, block_size, hq, hkv)
+    if need == 0:
+        raise RuntimeError("train_attn_bwd: unsupported shape")
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = load().train_attn_bwd(D3D_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(anchors), L,
+                               n_blocks, block_size, hq, hkv, d, float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                               need, _stream(stream))
+    _check(st, "train_attn_bwd")
+    return dq, dk, dv

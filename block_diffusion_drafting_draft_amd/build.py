@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libd3d.so")
-SOURCES = ["attn.hip", "verify.hip", "match.hip", "select.hip", "commit.hip", "awl.hip"]
+SOURCES = ["attn.hip", "verify.hip", "match.hip", "select.hip", "commit.hip", "awl.hip", "train_attn.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -21,9 +21,15 @@ import statistics
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+KERNEL_SOURCES = ("attn.hip", "attn_tiles.h")  # the attention kernel's source text
+
+
 def source_digest():
-    with open(os.path.join(ROOT, "csrc", "attn.hip"), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def per_dispatch(path, counter, name_part):

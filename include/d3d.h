@@ -260,6 +260,36 @@ int awl_loss(d3d_dtype dtype, const void *target_logits, const void *draft_logit
              int n_pos, int vocab, double eps, float *weights, float *ce, double *loss, void *grad,
              void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Training-time packed attention ([D3D] 方法步骤详情 step 2, 核心方法; [DScout] 方法步骤详情 step 2).
+ * One response of L tokens followed by n_blocks diffusion blocks of block_size rows (block i at
+ * packed rows L + i*block_size .., its anchor at response position anchors[i]). A response row p
+ * attends to response keys j <= p; a row of block i attends to response keys j < anchors[i]
+ * (clamped to [0, L]) and to every row of block i; no row attends to another block. Query head h
+ * uses key / value head h / (n_heads_q / n_heads_kv).
+ *
+ *  q, out, dout, dq [N, n_heads_q, head_dim], k, v, dk, dv [N, n_heads_kv, head_dim] (bf16, DEVICE),
+ *  N = L + n_blocks * block_size; lse [N, n_heads_q] f32 DEVICE (natural log of the row's partition
+ *  sum of scale * q.k); anchors [n_blocks] int32 DEVICE. Blocks packed in increasing anchor order
+ *  run fastest (any order is computed correctly).
+ *  Supported: bf16, head_dim 128, (n_heads_q / n_heads_kv) dividing 32, n_blocks <= 2048,
+ *  N * n_heads_q * head_dim * 2 < 2^31 bytes; otherwise D3D_EUNSUPPORTED.
+ *  train_attn_fwd writes out and lse. train_attn_bwd takes the forward's out and lse and the upstream
+ *  gradient dout and writes dq, dk, dv (fp32 accumulation); ws: at least
+ *  train_attn_workspace(L, n_blocks, block_size, n_heads_q, n_heads_kv) bytes (per-row
+ *  rowsum(dout * out) and the fp32 partial key / value gradients of the query-tile chunks); no
+ *  initial contents required. train_attn_workspace returns 0 for an unsupported shape.
+ * Errors: D3D_EINVAL on bad sizes or NULL required pointers, D3D_EWORKSPACE, D3D_EUNSUPPORTED.
+ * ------------------------------------------------------------------------------------------- */
+size_t train_attn_workspace(int L, int n_blocks, int block_size, int n_heads_q, int n_heads_kv);
+int train_attn_fwd(d3d_dtype dtype, const void *q, const void *k, const void *v, const int32_t *anchors, int L,
+                   int n_blocks, int block_size, int n_heads_q, int n_heads_kv, int head_dim, float scale, void *out,
+                   float *lse, hipStream_t stream);
+int train_attn_bwd(d3d_dtype dtype, const void *q, const void *k, const void *v, const void *out, const void *dout,
+                   const float *lse, const int32_t *anchors, int L, int n_blocks, int block_size, int n_heads_q,
+                   int n_heads_kv, int head_dim, float scale, void *dq, void *dk, void *dv, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+
 const char *d3d_status_string(int status);
 
 #ifdef __cplusplus
