@@ -389,6 +389,13 @@ def awl_loss(target_logits, draft_logits, draft_tokens, labels, include=None, ep
                    ce=torch.empty((n_blocks, n_pos), dtype=torch.float32, device=dev))
         if grad:
             out["grad"] = torch.empty_like(draft_logits)
+    else:
+        _like(out["loss"], (1,), torch.float64, "loss")
+        _like(out["weights"], (n_blocks, n_pos), torch.float32, "weights")
+        if out.get("ce") is not None:
+            _like(out["ce"], (n_blocks, n_pos), torch.float32, "ce")
+        if out.get("grad") is not None:
+            _like(out["grad"], draft_logits.shape, draft_logits.dtype, "grad")
     need = awl_loss_workspace(n_blocks, n_pos, vocab)
     if need == 0:
         raise ValueError("unsupported awl_loss shape")
@@ -399,6 +406,14 @@ def awl_loss(target_logits, draft_logits, draft_tokens, labels, include=None, ep
                          _ptr(out["loss"]), _ptr(out.get("grad")), _ptr(ws), need, _stream(stream))
     _check(st, "awl_loss")
     return out
+
+
+def _like(t, shape, dtype, name):
+    """Check a caller-supplied tensor: contiguous, on the GPU, of this shape and dtype."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}")
+    return t
 
 
 def _train_shape(q, k, anchors, L, block_size):
@@ -423,10 +438,11 @@ def train_attn_fwd(q, k, v, anchors, L, block_size, scale=None, out=None, lse=No
     """Training-time packed attention forward. q [N, H_q, d], k, v [N, H_kv, d] bf16, anchors int32
     [n_blocks] (all on the GPU). Returns (out [N, H_q, d] bf16, lse [N, H_q] f32)."""
     n_blocks, N, hq, hkv, d = _train_shape(q, k, anchors, L, block_size)
-    _dev(v, "v")
+    _like(v, k.shape, torch.bfloat16, "v")
     scale = d ** -0.5 if scale is None else scale
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((N, hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    out = torch.empty_like(q) if out is None else _like(out, q.shape, torch.bfloat16, "out")
+    lse = (torch.empty((N, hq), dtype=torch.float32, device=q.device) if lse is None
+           else _like(lse, (N, hq), torch.float32, "lse"))
     st = load().train_attn_fwd(D3D_BF16, _ptr(q), _ptr(k), _ptr(v), _ptr(anchors), L, n_blocks, block_size, hq, hkv, d,
                                float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "train_attn_fwd")
@@ -438,12 +454,14 @@ def train_attn_bwd(q, k, v, out, dout, lse, anchors, L, block_size, scale=None, 
     """Training-time packed attention backward: (dq, dk, dv) from the forward's out, lse and the
     upstream gradient dout (bf16 tensors on the GPU)."""
     n_blocks, N, hq, hkv, d = _train_shape(q, k, anchors, L, block_size)
-    for t, n in ((v, "v"), (out, "out"), (dout, "dout"), (lse, "lse")):
-        _dev(t, n)
+    _like(v, k.shape, torch.bfloat16, "v")
+    for t, n in ((out, "out"), (dout, "dout")):
+        _like(t, q.shape, torch.bfloat16, n)
+    _like(lse, (N, hq), torch.float32, "lse")
     scale = d ** -0.5 if scale is None else scale
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _like(dq, q.shape, torch.bfloat16, "dq")
+    dk = torch.empty_like(k) if dk is None else _like(dk, k.shape, torch.bfloat16, "dk")
+    dv = torch.empty_like(v) if dv is None else _like(dv, k.shape, torch.bfloat16, "dv")
     need = train_attn_workspace(L, n_blocks, block_size, hq, hkv)
     if need == 0:
         raise RuntimeError("train_attn_bwd: unsupported shape")

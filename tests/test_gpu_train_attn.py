@@ -158,3 +158,5 @@ def test_train_attention_bad_arguments():
     q3 = torch.zeros((48, 6, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError):  # 3 heads per group does not divide 32
         _binding.train_attn_fwd(q3, k, k, an, 16, 16)
+    with pytest.raises(ValueError):  # an output of the wrong shape is refused before any launch
+        _binding.train_attn_fwd(q, k, k, an, 16, 16, out=torch.zeros((40, 8, 128), dtype=torch.bfloat16, device="cuda"))
