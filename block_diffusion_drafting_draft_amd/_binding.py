@@ -39,6 +39,10 @@ _SIGNATURES = {
                                _c.c_int, _c.c_float, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
                                _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                _c.c_size_t, _c.c_void_p]),
+    "spec_verify_match": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                                     _c.c_int, _c.c_float, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
+                                     _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                     _c.c_size_t, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "branch_cache_match": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "draft_topk_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
@@ -231,10 +235,12 @@ def spec_verify_workspace(n_req, n_draft, vocab):
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, round_, ws=None, out=None,
-                stream=None):
+                stream=None, match=None):
     """Speculative-sampling verify. target_logits [n_req, B, V], draft_logits [n_req, B-1, V],
     draft_tokens int32 [n_req, B-1]. Returns a dict of device tensors: n_accepted, next_token, alpha,
-    survival, tau, flags."""
+    survival, tau, flags. With match=(descs, req_block_off) (int32 GPU tensors as for
+    branch_cache_match) the cache match runs inside the verify launches (spec_verify_match) and the
+    dict also holds hit_branch."""
     _dev(target_logits, "target_logits")
     _dev(draft_tokens, "draft_tokens")
     dt = _dtype_code(target_logits)
@@ -259,12 +265,25 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, ro
         raise ValueError("unsupported verify shape")
     if ws is None or ws.numel() * ws.element_size() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    st = load().spec_verify(dt, _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), n_req, nd, vocab,
-                            float(temperature), int(seed) & (2**64 - 1), int(round_) & 0xFFFFFFFF,
-                            _ptr(out["n_accepted"]), _ptr(out["next_token"]), _ptr(out["alpha"]),
-                            _ptr(out["survival"]), _ptr(out["tau"]), _ptr(out["flags"]), _ptr(ws), need,
-                            _stream(stream))
-    _check(st, "spec_verify")
+    args = (dt, _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), n_req, nd, vocab, float(temperature),
+            int(seed) & (2**64 - 1), int(round_) & 0xFFFFFFFF, _ptr(out["n_accepted"]), _ptr(out["next_token"]),
+            _ptr(out["alpha"]), _ptr(out["survival"]), _ptr(out["tau"]), _ptr(out["flags"]), _ptr(ws), need)
+    if match is None:
+        st = load().spec_verify(*args, _stream(stream))
+        _check(st, "spec_verify")
+        return out
+    descs, req_block_off = match
+    for t, n in ((descs, "descs"), (req_block_off, "req_block_off")):
+        _dev(t, n)
+        if t.dtype != torch.int32:
+            raise TypeError(f"{n} must be int32")
+    if req_block_off.numel() != n_req + 1:
+        raise ValueError("req_block_off must have n_req + 1 entries")
+    if out.get("hit_branch") is None:
+        out["hit_branch"] = torch.empty(n_req, dtype=torch.int32, device=dev)
+    st = load().spec_verify_match(*args, _ptr(descs), descs.shape[0], _ptr(req_block_off), _ptr(out["hit_branch"]),
+                                  _stream(stream))
+    _check(st, "spec_verify_match")
     return out
 
 

@@ -103,6 +103,25 @@ __device__ __forceinline__ double exp_fp64(double x) {
   return ldexp(p, static_cast<int>(k));
 }
 
+// Cache match of one request ([D3D] 前置知识: 异步起草与缓存命中), run by one whole wavefront (every
+// lane gets the result): the first branch block b of [b0 + 1, b1) in pack order whose rejection
+// position is n_acc + 1 and whose anchor is the verified next token, as b - b0, or -1. Lanes test 64
+// consecutive blocks at a time; the lowest matching lane of the first window with one wins.
+__device__ __forceinline__ int match_request(const d3d_block_desc *descs, int b0, int b1, int want_r, int tok) {
+  const int lane = threadIdx.x & 63;
+  for (int base = b0 + 1; base < b1; base += 64) {
+    const int b = base + lane;
+    bool m = false;
+    if (b < b1) {
+      const d3d_block_desc d = descs[b];
+      m = d.rej_pos == want_r && d.anchor == tok;
+    }
+    const unsigned long long bal = __ballot(m);
+    if (bal) return base + (__ffsll(static_cast<long long>(bal)) - 1) - b0;
+  }
+  return -1;
+}
+
 inline int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? D3D_OK : D3D_EHIP;

@@ -11,8 +11,7 @@
 namespace d3d {
 namespace {
 
-// One wavefront per request: lanes test 64 consecutive blocks at a time; the lowest matching lane
-// of the first window that has one is the first hit in pack order.
+// One wavefront per request.
 __global__ __launch_bounds__(256) void match_kernel(const d3d_block_desc *descs, int total_blocks,
                                                     const int32_t *off, int n_req,
                                                     const int32_t *n_acc, const int32_t *next,
@@ -22,22 +21,7 @@ __global__ __launch_bounds__(256) void match_kernel(const d3d_block_desc *descs,
   if (i >= n_req) return;
   const int b0 = min(max(off[i], 0), total_blocks);
   const int b1 = min(max(off[i + 1], b0), total_blocks);
-  const int want_r = n_acc[i] + 1;
-  const int tok = next[i];
-  int found = -1;
-  for (int base = b0 + 1; base < b1; base += 64) {
-    const int b = base + lane;
-    bool m = false;
-    if (b < b1) {
-      const d3d_block_desc d = descs[b];
-      m = d.rej_pos == want_r && d.anchor == tok;
-    }
-    const unsigned long long bal = __ballot(m);
-    if (bal) {
-      found = base + (__ffsll(static_cast<long long>(bal)) - 1) - b0;
-      break;
-    }
-  }
+  const int found = match_request(descs, b0, b1, n_acc[i] + 1, next[i]);
   if (lane == 0) hit[i] = found;
 }
 

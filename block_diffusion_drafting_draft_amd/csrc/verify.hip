@@ -87,7 +87,20 @@ struct VerifyArgs {
   SampleState *state;
   double *lse_part;   // [n_req][s_chunks][2]
   double *mass_part;  // [n_req][s_chunks]
+  // optional cache match of the verified outcome against the round's branch descriptors
+  const d3d_block_desc *descs;
+  const int32_t *req_block_off;
+  int total_blocks;
+  int32_t *hit;
 };
+
+// The cache match of request i once its outcome is known (one whole wavefront).
+__device__ __forceinline__ void match_outcome(const VerifyArgs &a, int i, int n_acc, int tok) {
+  const int b0 = min(max(a.req_block_off[i], 0), a.total_blocks);
+  const int b1 = min(max(a.req_block_off[i + 1], b0), a.total_blocks);
+  const int found = match_request(a.descs, b0, b1, n_acc + 1, tok);
+  if ((threadIdx.x & 63) == 0) a.hit[i] = found;
+}
 
 // ------------------------------------------------------------------------------------------------
 // block reductions (256 threads = 4 wavefronts)
@@ -415,6 +428,8 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
       }
     }
   }
+  // greedy: the outcome is final here (sampling matches after its draw)
+  if (store && a.greedy && a.hit) match_outcome(a, i, n_acc, rr.arg[n_acc]);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -631,7 +646,7 @@ __device__ __forceinline__ Found chunk_find(const DrawRows<T> &d, int c, int V, 
 // The draw of request i from its chunk masses: chunk prefix, the chunk holding u'Z, then the
 // in-chunk scan.
 template <typename T, bool VEC>
-__device__ __forceinline__ void draw_token(const VerifyArgs &a, int i, const SampleState &st, DrawRows<T> d,
+__device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const SampleState &st, DrawRows<T> d,
                                            double *sh_d, int *sh_i, double *sh_cum, Found *sh_found) {
   constexpr int CPT = kMaxSampleChunks / kThreads;  // each thread owns 4 consecutive chunks
   const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
@@ -689,6 +704,7 @@ __device__ __forceinline__ void draw_token(const VerifyArgs &a, int i, const Sam
     a.next_token[i] = f.v;
     if (a.flags) a.flags[i] |= fl;
   }
+  return f.v;
 }
 
 // Residual (or bonus) mass of one 2048-token chunk.
@@ -723,7 +739,8 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs 
   if (st.mode == kDone) return;
   DrawRows<T> d = draw_rows_base<T>(a, st);
   finish_draw_rows(a, i, d, sh_d);
-  draw_token<T, VEC>(a, i, st, d, sh_d, sh_i, sh_cum, &sh_found);
+  const int tok = draw_token<T, VEC>(a, i, st, d, sh_d, sh_i, sh_cum, &sh_found);
+  if (a.hit && threadIdx.x < 64) match_outcome(a, i, st.tgt_row - i * (a.n_draft + 1), tok);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -795,12 +812,13 @@ extern "C" size_t spec_verify_workspace(int n_req, int n_draft, int vocab) {
   return p.total;
 }
 
-extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
-                           const int32_t *draft_tokens, int n_req, int n_draft, int vocab,
-                           float temperature, uint64_t seed, uint32_t round, int32_t *n_accepted,
-                           int32_t *next_token, float *alpha, float *survival, float *tau,
-                           uint32_t *flags, void *ws, size_t ws_bytes, hipStream_t stream) {
-  using namespace d3d;
+namespace d3d {
+namespace {
+int verify_impl(d3d_dtype dtype, const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                int n_req, int n_draft, int vocab, float temperature, uint64_t seed, uint32_t round,
+                int32_t *n_accepted, int32_t *next_token, float *alpha, float *survival, float *tau, uint32_t *flags,
+                void *ws, size_t ws_bytes, const d3d_block_desc *descs, int total_blocks,
+                const int32_t *req_block_off, int32_t *hit, hipStream_t stream) {
   if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
   if (!target_logits || !draft_tokens || !n_accepted || !next_token) return D3D_EINVAL;
   if (!(temperature >= 0.f) || !isfinite(temperature)) return D3D_EINVAL;
@@ -836,6 +854,10 @@ extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const voi
   a.state = reinterpret_cast<SampleState *>(w + p.off_state);
   a.lse_part = reinterpret_cast<double *>(w + p.off_lse);
   a.mass_part = reinterpret_cast<double *>(w + p.off_mass);
+  a.descs = descs;
+  a.req_block_off = req_block_off;
+  a.total_blocks = total_blocks;
+  a.hit = hit;
   const size_t esize = dtype == D3D_BF16 ? 2 : 4;
   const size_t width = 16 / esize;
   const bool aligned = (reinterpret_cast<uintptr_t>(target_logits) % 16 == 0) &&
@@ -844,4 +866,28 @@ extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const voi
   if (dtype == D3D_BF16)
     return vec ? launch_verify<__bf16, true>(a, stream) : launch_verify<__bf16, false>(a, stream);
   return vec ? launch_verify<float, true>(a, stream) : launch_verify<float, false>(a, stream);
+}
+}  // namespace
+}  // namespace d3d
+
+extern "C" int spec_verify(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                           const int32_t *draft_tokens, int n_req, int n_draft, int vocab,
+                           float temperature, uint64_t seed, uint32_t round, int32_t *n_accepted,
+                           int32_t *next_token, float *alpha, float *survival, float *tau,
+                           uint32_t *flags, void *ws, size_t ws_bytes, hipStream_t stream) {
+  return d3d::verify_impl(dtype, target_logits, draft_logits, draft_tokens, n_req, n_draft, vocab, temperature, seed,
+                          round, n_accepted, next_token, alpha, survival, tau, flags, ws, ws_bytes, nullptr, 0,
+                          nullptr, nullptr, stream);
+}
+
+extern "C" int spec_verify_match(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                                 const int32_t *draft_tokens, int n_req, int n_draft, int vocab, float temperature,
+                                 uint64_t seed, uint32_t round, int32_t *n_accepted, int32_t *next_token,
+                                 float *alpha, float *survival, float *tau, uint32_t *flags, void *ws,
+                                 size_t ws_bytes, const d3d_block_desc *descs, int total_blocks,
+                                 const int32_t *req_block_off, int32_t *hit_branch, hipStream_t stream) {
+  if (!descs || !req_block_off || !hit_branch || total_blocks < 1) return D3D_EINVAL;
+  return d3d::verify_impl(dtype, target_logits, draft_logits, draft_tokens, n_req, n_draft, vocab, temperature, seed,
+                          round, n_accepted, next_token, alpha, survival, tau, flags, ws, ws_bytes, descs,
+                          total_blocks, req_block_off, hit_branch, stream);
 }

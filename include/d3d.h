@@ -187,6 +187,21 @@ int branch_cache_match(const d3d_block_desc *descs, int total_blocks, const int3
                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * spec_verify followed by branch_cache_match on its outcome, in the same launches: the match of a
+ * request runs in the pass that settles its next token (greedy: the decide pass; sampling: the draw
+ * pass). Arguments as spec_verify, then the branch_cache_match arguments (descs [total_blocks],
+ * req_block_off DEVICE [n_req+1], hit_branch [n_req]). Outputs are identical to the two calls in
+ * sequence. Errors: as spec_verify, and D3D_EINVAL on NULL descs / req_block_off / hit_branch or
+ * total_blocks < 1.
+ * ------------------------------------------------------------------------------------------- */
+int spec_verify_match(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                      const int32_t *draft_tokens, int n_req, int n_draft, int vocab, float temperature,
+                      uint64_t seed, uint32_t round, int32_t *n_accepted, int32_t *next_token, float *alpha,
+                      float *survival, float *tau, uint32_t *flags, void *ws, size_t ws_bytes,
+                      const d3d_block_desc *descs, int total_blocks, const int32_t *req_block_off,
+                      int32_t *hit_branch, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Drafter token selection ([D3D] 方法步骤详情 step 4, 前置知识: 异步起草与缓存命中): the k best
  * tokens of each logit row other than an excluded one. Order: larger logit first, ties to the lower
  * token id; NaN logits count as -inf. Uses: the greedy drafted token of every masked position of the

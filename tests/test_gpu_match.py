@@ -136,3 +136,43 @@ def test_graph_replays_match_eager():
             assert torch.equal(a, b), rep
         device_round()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.0])
+def test_fused_verify_match_equals_the_two_calls(temperature):
+    """spec_verify_match gives exactly spec_verify followed by branch_cache_match: 16 requests whose
+    branch lists are built (from a first verify of the same inputs) so that some hold the verified
+    outcome at various positions and the others miss."""
+    require_gpu()
+    _say(f"fused verify + match, T = {temperature}")
+    w = synth.WORKLOADS["serve-16req-B16C12F2-paged16-V151936"]
+    vin = synth.verify_inputs(w, vocab=8192, temperature=temperature)
+    zt, zd = dev(vin["z_target"], "bf16"), dev(vin["z_draft"], "bf16")
+    tok = torch.from_numpy(vin["tokens"]).cuda()
+    first = _binding.spec_verify(zt, zd, tok, temperature, vin["philox_seed"], 5)
+    n_acc = first["n_accepted"].cpu().numpy()
+    nxt = first["next_token"].cpu().numpy()
+    B, C, F = w.block_size, w.coverage, w.fanout
+    rng = np.random.default_rng(3)
+    descs, off = [], [0]
+    for i in range(w.n_req):
+        anchors = rng.integers(0, 8192, size=(C - 1) * F + 1).astype(np.int32)
+        k = int(n_acc[i]) + 1
+        if i % 3 != 2 and k <= C - 1:  # plant the outcome at rejection position k (fan-out slot i % F)
+            anchors[(k - 1) * F + i % F] = nxt[i]
+        elif i % 3 != 2 and k == B:  # full accept: the full-accept branch's anchor
+            anchors[(C - 1) * F] = nxt[i]
+        d = _binding.d3d_build_branch_descs(B, C, F, 1000 + i, int(rng.integers(0, 8192)), anchors)
+        descs.append(d)
+        off.append(off[-1] + len(d))
+    descs_d = torch.from_numpy(np.ascontiguousarray(np.concatenate(descs), np.int32)).cuda()
+    off_d = torch.tensor(off, dtype=torch.int32, device="cuda")
+    sep = _binding.spec_verify(zt, zd, tok, temperature, vin["philox_seed"], 5)
+    hit_sep = _binding.branch_cache_match(descs_d, off_d, sep["n_accepted"], sep["next_token"])
+    fused = _binding.spec_verify(zt, zd, tok, temperature, vin["philox_seed"], 5, match=(descs_d, off_d))
+    torch.cuda.synchronize()
+    for key in ("n_accepted", "next_token", "alpha", "survival", "tau", "flags"):
+        assert torch.equal(fused[key], sep[key]), key
+    assert torch.equal(fused["hit_branch"], hit_sep)
+    h = hit_sep.cpu().numpy()
+    assert (h >= 0).sum() >= 4 and (h == -1).sum() >= 2, h
