@@ -48,7 +48,8 @@ def parse():
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss",
-                                     "train_attn_fwd", "train_attn_bwd"),
+                                     "train_attn_fwd", "train_attn_bwd", "draft_topk_tokens", "draft_topk_anchors",
+                                     "kv_commit"),
                    default=None,
                    help="only replay this call's graph (warmup + steps times, nothing else on the GPU) and print "
                         "its event-timed duration: the command to profile one call's kernels alone")
@@ -272,6 +273,14 @@ def main():
     if args.call:
         if args.call == "awl_loss":
             g = awl_graph(r, torch)[0]
+        elif args.call in ("draft_topk_tokens", "draft_topk_anchors"):
+            tg = topk_graphs(r, torch)
+            if tg is None:
+                print("this workload drafts no branches", file=sys.stderr)
+                return 2
+            g = tg[args.call.rsplit("_", 1)[1]][0]
+        elif args.call == "kv_commit":
+            g = next_row_commit(r, torch, None, graph_only=True)
         elif args.call in ("train_attn_fwd", "train_attn_bwd"):
             g = train_attn_graphs(r, torch)[0 if args.call == "train_attn_fwd" else 1]
         else:
@@ -526,7 +535,7 @@ def next_row_awl(r, torch, mean_us):
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
-def next_row_commit(r, torch, mean_us):
+def next_row_commit(r, torch, mean_us, graph_only=False):
     """KV commit (the second next row, not part of the step): each request's accepted slice (n_acc + 1
     rows of block 0, n_acc from this round's verify outputs) appended to a paged cache at the end of
     its prefix, plus promotion of the hit branch. The page table maps the pages around each prefix
@@ -561,6 +570,9 @@ def next_row_commit(r, torch, mean_us):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         fn()
+    g.keep = (lens0, table, kc, vc, lens, tokens, nxt, status)
+    if graph_only:
+        return g
     t = mean_us(g, 100)
     rows = int((n_acc.clamp(0, B - 1) + 1).sum().item())
     nbytes = rows * hkv * d * r.k_new.element_size() * 2 * 2
@@ -568,11 +580,12 @@ def next_row_commit(r, torch, mean_us):
             "note": "graph also restores the prefix lengths (one small device copy)"}
 
 
-def next_row_topk(r, torch, cur, mean_us):
-    """Drafter token selection (the first next row, not part of the step): greedy tokens of every
-    masked position of the packed blocks (k = 1 over rows of drafter logits; synthetic N(0, 3) bf16
-    logits drawn on the device: timing only) and the branch anchors in the builder's layout (top-F of
-    draft rows 1..C-1 excluding the drafts, then the full-accept anchor). HBM bytes = rows x V x 2."""
+def topk_graphs(r, torch):
+    """Graphs of drafter token selection: greedy tokens of every masked position of the packed blocks
+    (k = 1 over rows of drafter logits; synthetic N(0, 3) bf16 logits drawn on the device: timing
+    only) and the branch anchors in the builder's layout (top-F of draft rows 1..C-1 excluding the
+    drafts, then the full-accept anchor). Returns {"tokens" | "anchors": (graph, rows read)}, or None
+    for workloads without branches."""
     w, lib = r.w, r.lib
     if not w.coverage or w.dtype != "bf16":
         return None
@@ -603,18 +616,31 @@ def next_row_topk(r, torch, cur, mean_us):
         lib.draft_topk(zd_rows, F, rows=rows, exclude=excl, out=alt, out_off=offs, ws=ws_a)
         lib.draft_topk(z_next, 1, out=alt, out_off=offs_full, ws=ws_a)
 
-    res = {}
+    out = {}
     for name, fn, n_rows in (("tokens", tokens, masked.numel()), ("anchors", anchors, rows.numel() + n_req)):
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
+        g.keep = (logits, masked, toks, rows, excl, offs, offs_full, z_next, alt, ws_t, ws_a)
+        out[name] = (g, int(n_rows))
+    return out
+
+
+def next_row_topk(r, torch, cur, mean_us):
+    """Drafter token selection (the first next row, not part of the step), timed as the mean of
+    back-to-back graph replays. HBM bytes = rows x V x 2."""
+    graphs = topk_graphs(r, torch)
+    if graphs is None:
+        return None
+    V = r.w.vocab
+    res = {}
+    for name, (g, n_rows) in graphs.items():
         t = mean_us(g, 100)
         nbytes = n_rows * V * 2
         res[name] = {"rows": int(n_rows), "us": round(t, 3), "gbs": round(nbytes / (t * 1e-6) / 1e9, 1),
                      "pct_hbm_peak": round(100 * nbytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
-    del logits
     return res
 
 

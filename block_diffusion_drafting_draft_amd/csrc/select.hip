@@ -256,10 +256,17 @@ int plan_select(int n_rows, int vocab, int k, SelPlan *p) {
 
 template <typename T, bool VEC>
 void launch_select(const SelArgs &a, hipStream_t stream) {
+  // per-thread lists just deep enough for k (a thread's share of the k best is at most k elements)
   const dim3 grid(a.chunks, a.n_rows);
   if (a.k == 1) {
     topk_chunk_kernel<T, VEC, 1><<<grid, kThreads, 0, stream>>>(a);
     topk_merge_kernel<1><<<a.n_rows, kThreads, 0, stream>>>(a);
+  } else if (a.k == 2) {
+    topk_chunk_kernel<T, VEC, 2><<<grid, kThreads, 0, stream>>>(a);
+    topk_merge_kernel<2><<<a.n_rows, kThreads, 0, stream>>>(a);
+  } else if (a.k <= 4) {
+    topk_chunk_kernel<T, VEC, 4><<<grid, kThreads, 0, stream>>>(a);
+    topk_merge_kernel<4><<<a.n_rows, kThreads, 0, stream>>>(a);
   } else {
     topk_chunk_kernel<T, VEC, kSelMaxK><<<grid, kThreads, 0, stream>>>(a);
     topk_merge_kernel<kSelMaxK><<<a.n_rows, kThreads, 0, stream>>>(a);
