@@ -114,6 +114,7 @@ class Round:
         need = _binding.draft_attn_packed_workspace(self.q.dtype, self.off, self.lens, self.B, self.q.shape[1],
                                                     self.k_new.shape[1], self.q.shape[2])
         self.attn_ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        self.attn_merges = need > 0  # split partials: the call ends with its merge launch
         nd = self.B - 1
         self.ver_ws = torch.empty(_binding.spec_verify_workspace(self.n_req, nd, w.vocab), dtype=torch.uint8,
                                   device="cuda")
@@ -138,10 +139,10 @@ class Round:
         if pinned is None:
             self.descs.copy_(self.desc_host, non_blocking=True)
 
-    def attention(self):
+    def attention(self, join=None):
         self.lib.draft_attn_packed(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.descs,
                                    self.off, self.lens_i32, self.B, page_table=self.page_table,
-                                   page_size=self.w.page_size, out=self.out, ws=self.attn_ws)
+                                   page_size=self.w.page_size, out=self.out, ws=self.attn_ws, join=join)
 
     def verify(self, match=False):
         """spec_verify; with match=True the cache match runs inside it (spec_verify_match)."""
@@ -242,20 +243,28 @@ def main():
     copied = [torch.cuda.Event() for _ in ring]
 
     side = torch.cuda.Stream()  # default priority
+    verified = torch.cuda.Event()
 
     def device_round():
         # The drafter's packed attention (branches for the next block) and the target's verify of the
-        # current block are independent within a round: they run on two streams, and the cache match,
-        # which needs the verify outcome and the branch descriptors, joins them. (Running the match
-        # inside the verify launches, spec_verify_match, and ending the graph on the join measured
-        # slower: 77 vs 70 µs a round at async.)
+        # current block are independent within a round: they run on two streams. The cache match needs
+        # the verify outcome and the branch descriptors (built before the round), not the drafted
+        # branches. When the attention ends with its split merge, the match runs inside the verify
+        # launches (spec_verify_match) and the attention stream joins the verify stream just before
+        # the merge launch (draft_attn_packed_join): the round ends with that kernel. Without a merge,
+        # the match kernel follows the join (a graph that ends on a bare join measured slower).
         cur = torch.cuda.current_stream()
         side.wait_stream(cur)
         with torch.cuda.stream(side):
-            r.verify()
-        r.attention()
-        cur.wait_stream(side)
-        r.match()
+            r.verify(match=r.attn_merges)
+            verified.record(side)
+        if r.attn_merges:
+            r.attention(join=verified)
+            cur.wait_stream(side)
+        else:
+            r.attention()
+            cur.wait_stream(side)
+            r.match()
 
     for _ in range(3):  # eager warm-up (first launches, code-object loads)
         r.build_descs()

@@ -34,6 +34,11 @@ _SIGNATURES = {
                                      _c.c_void_p, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                      _c.c_int, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_size_t,
                                      _c.c_void_p]),
+    "draft_attn_packed_join": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                          _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                          _c.c_void_p, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                          _c.c_int, _c.c_float, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                          _c.c_void_p, _c.c_void_p]),
     "spec_verify_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
     "spec_verify": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
                                _c.c_int, _c.c_float, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
@@ -173,10 +178,12 @@ def draft_attn_packed_workspace(dtype, req_block_off, req_prefix_len, block_size
 
 def draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, req_prefix_len, block_size,
                       scale=None, page_table=None, page_size=16, kv_stride=None, out=None, ws=None,
-                      stream=None):
+                      stream=None, join=None):
     """Packed draft attention. q [N_q, H_q, d]; k_new/v_new [N_q, H_kv, d]; k_cache/v_cache either
     [n_req, kv_stride, H_kv, d] (page_table None) or [n_pages, page_size, H_kv, d]; descs: device int32
-    [n_blocks, 4]; req_block_off / req_prefix_len: host ints. Returns out [N_q, H_q, d]."""
+    [n_blocks, 4]; req_block_off / req_prefix_len: host ints. Returns out [N_q, H_q, d]. join: a
+    recorded torch.cuda.Event the stream waits for before the call's last launch
+    (draft_attn_packed_join)."""
     for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (descs, "descs")):
         _dev(t, n)
     dt = _dtype_code(q)
@@ -221,11 +228,14 @@ def draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, r
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     scale = d ** -0.5 if scale is None else scale
-    st = load().draft_attn_packed(dt, _ptr(q), _ptr(k_new), _ptr(v_new),
-                                  _ptr(k_cache) if has_prefix else None, _ptr(v_cache) if has_prefix else None,
-                                  _ptr(page_table), page_size, max_pages, num_pages, stride,
-                                  _ptr(descs), off_p, pre_p, n_req, block_size, hq, hkv, d, float(scale),
-                                  _ptr(out), _ptr(ws) if need else None, need, _stream(stream))
+    args = (dt, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache) if has_prefix else None,
+            _ptr(v_cache) if has_prefix else None, _ptr(page_table), page_size, max_pages, num_pages, stride,
+            _ptr(descs), off_p, pre_p, n_req, block_size, hq, hkv, d, float(scale), _ptr(out),
+            _ptr(ws) if need else None, need)
+    if join is None:
+        st = load().draft_attn_packed(*args, _stream(stream))
+    else:
+        st = load().draft_attn_packed_join(*args, join.cuda_event, _stream(stream))
     _check(st, "draft_attn_packed")
     return out
 

@@ -865,7 +865,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
 }
 
 template <typename T, int D>
-void launch(const AttnPlan &P, bool paged, hipStream_t stream) {
+void launch(const AttnPlan &P, bool paged, hipEvent_t join, hipStream_t stream) {
   if (P.args.n_groups > 0) {
     if constexpr (Cfg<T>::kBf16) {
       // rows one DMA instruction covers: 64 / (D / 8)
@@ -882,6 +882,7 @@ void launch(const AttnPlan &P, bool paged, hipStream_t stream) {
         attn_kernel_f32<D, false><<<P.grid, kThreads, 0, stream>>>(P.args);
     }
   }
+  if (join) (void)hipStreamWaitEvent(stream, join, 0);  // the caller's other stream joins here
   if (P.args.comb_rows > 0) combine_kernel<T, D><<<P.comb_grid, kThreads, 0, stream>>>(P.args);
 }
 
@@ -899,13 +900,13 @@ extern "C" size_t draft_attn_packed_workspace(d3d_dtype dtype, const int32_t *re
   return P.ws_bytes;
 }
 
-extern "C" int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_new, const void *v_new,
-                                 const void *k_cache, const void *v_cache, const int32_t *page_table,
-                                 int page_size, int max_pages, int num_pages, int kv_stride,
-                                 const d3d_block_desc *descs, const int32_t *req_block_off,
-                                 const int32_t *req_prefix_len, int n_req, int block_size, int n_heads_q,
-                                 int n_heads_kv, int head_dim, float scale, void *out, void *ws,
-                                 size_t ws_bytes, hipStream_t stream) {
+extern "C" int draft_attn_packed_join(d3d_dtype dtype, const void *q, const void *k_new, const void *v_new,
+                                      const void *k_cache, const void *v_cache, const int32_t *page_table,
+                                      int page_size, int max_pages, int num_pages, int kv_stride,
+                                      const d3d_block_desc *descs, const int32_t *req_block_off,
+                                      const int32_t *req_prefix_len, int n_req, int block_size, int n_heads_q,
+                                      int n_heads_kv, int head_dim, float scale, void *out, void *ws,
+                                      size_t ws_bytes, hipEvent_t join, hipStream_t stream) {
   using namespace d3d;
   if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
   AttnPlan P;
@@ -952,14 +953,26 @@ extern "C" int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_n
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   if (dtype == D3D_BF16) {
     if (head_dim == 128)
-      launch<__bf16, 128>(P, paged, stream);
+      launch<__bf16, 128>(P, paged, join, stream);
     else
-      launch<__bf16, 64>(P, paged, stream);
+      launch<__bf16, 64>(P, paged, join, stream);
   } else {
     if (head_dim == 128)
-      launch<float, 128>(P, paged, stream);
+      launch<float, 128>(P, paged, join, stream);
     else
-      launch<float, 64>(P, paged, stream);
+      launch<float, 64>(P, paged, join, stream);
   }
   return launch_status();
+}
+
+extern "C" int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_new, const void *v_new,
+                                 const void *k_cache, const void *v_cache, const int32_t *page_table,
+                                 int page_size, int max_pages, int num_pages, int kv_stride,
+                                 const d3d_block_desc *descs, const int32_t *req_block_off,
+                                 const int32_t *req_prefix_len, int n_req, int block_size, int n_heads_q,
+                                 int n_heads_kv, int head_dim, float scale, void *out, void *ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  return draft_attn_packed_join(dtype, q, k_new, v_new, k_cache, v_cache, page_table, page_size, max_pages, num_pages,
+                                kv_stride, descs, req_block_off, req_prefix_len, n_req, block_size, n_heads_q,
+                                n_heads_kv, head_dim, scale, out, ws, ws_bytes, nullptr, stream);
 }

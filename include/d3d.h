@@ -136,6 +136,19 @@ int draft_attn_packed(d3d_dtype dtype, const void *q, const void *k_new, const v
                       int n_heads_kv, int head_dim, float scale, void *out, void *ws,
                       size_t ws_bytes, hipStream_t stream);
 
+/* draft_attn_packed with a join: before its last launch (the split merge, when the call has one:
+ * draft_attn_packed_workspace > 0; otherwise after the attention kernel) the stream waits for the
+ * event `join` (hipStreamWaitEvent). A round that verifies on a second stream while the drafter
+ * attends joins the two there, so that the merge is the round's last kernel. join == NULL is
+ * draft_attn_packed. Same arguments, outputs and errors otherwise. */
+int draft_attn_packed_join(d3d_dtype dtype, const void *q, const void *k_new, const void *v_new,
+                           const void *k_cache, const void *v_cache, const int32_t *page_table,
+                           int page_size, int max_pages, int num_pages, int kv_stride,
+                           const d3d_block_desc *descs, const int32_t *req_block_off,
+                           const int32_t *req_prefix_len, int n_req, int block_size, int n_heads_q,
+                           int n_heads_kv, int head_dim, float scale, void *out, void *ws,
+                           size_t ws_bytes, hipEvent_t join, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Speculative-sampling verify ([D3D] 前置知识: 投机解码; [DScout] 前置知识: 推测解码, 平均接受长度
  * MAT, 接受加权损失 AWL 与推测采样接受规则).

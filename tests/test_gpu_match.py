@@ -176,3 +176,60 @@ def test_fused_verify_match_equals_the_two_calls(temperature):
     assert torch.equal(fused["hit_branch"], hit_sep)
     h = hit_sep.cpu().numpy()
     assert (h >= 0).sum() >= 4 and (h == -1).sum() >= 2, h
+
+
+def test_round_with_join_equals_sequential_calls():
+    """The round as the bench runs it when the attention merges splits: verify + match on a second
+    stream, the attention stream joining it before its merge launch (draft_attn_packed_join). Outputs
+    equal the plain calls in sequence, eagerly and on graph replays."""
+    require_gpu()
+    _say("two-stream round with the join before the merge")
+    B, C, F, L = 16, 4, 2, 3000
+    w = synth.Workload("join", "bf16", 32, 8, 128, B, C, F, (L,), 1, False, 4096, "zipf", 0.8, 1.0, 23, 0x79)
+    ain, vin = synth.attention_inputs(w), synth.verify_inputs(w)
+    prob = AttnProblem("bf16", B, [dict(L=L, kind="async", C=C, F=F, a0=int(vin["cur_anchor"][0]),
+                                        anchors=vin["alt_anchors"][0])], ain)
+    need = _binding.draft_attn_packed_workspace("bf16", prob.off, prob.pre, B, 32, 8, 128)
+    assert need > 0  # the call merges splits
+    zt, zd = dev(vin["z_target"], "bf16"), dev(vin["z_draft"], "bf16")
+    tok = torch.from_numpy(vin["tokens"]).cuda()
+    off_dev = torch.tensor(prob.off, dtype=torch.int32).cuda()
+    ref_out = _binding.draft_attn_packed(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.descs,
+                                         prob.off, prob.pre, B)
+    ref = _binding.spec_verify(zt, zd, tok, 1.0, 0x79, 2)
+    ref_hit = _binding.branch_cache_match(prob.descs, off_dev, ref["n_accepted"], ref["next_token"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    out = torch.empty_like(prob.q)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    res = {}
+
+    def round_():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            res.update(_binding.spec_verify(zt, zd, tok, 1.0, 0x79, 2, out=res or None,
+                                            match=(prob.descs, off_dev)))
+            ev.record(side)
+        _binding.draft_attn_packed(prob.q, prob.k_new, prob.v_new, prob.k_cache, prob.v_cache, prob.descs,
+                                   prob.off, prob.pre, B, out=out, ws=ws, join=ev)
+        cur.wait_stream(side)
+
+    def check():
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        assert torch.equal(res["hit_branch"], ref_hit)
+        for k in ("n_accepted", "next_token", "alpha", "survival", "tau", "flags"):
+            assert torch.equal(res[k], ref[k]), k
+
+    round_()
+    check()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        round_()
+    for _ in range(3):
+        out.zero_()
+        res["hit_branch"].fill_(-7)
+        g.replay()
+        check()
