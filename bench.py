@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the next-row measurements (token selection, KV commit, AWL, training attention)")
     p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss",
                                      "train_attn_fwd", "train_attn_bwd", "draft_topk_tokens", "draft_topk_anchors",
                                      "kv_commit"),
@@ -442,10 +444,11 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},
     }
-    out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
-                        "kv_commit": next_row_commit(r, torch, mean_us),
-                        "awl_loss": next_row_awl(r, torch, mean_us),
-                        "train_attn": next_row_train_attn(r, torch, mean_us)}
+    if not args.no_next_rows:
+        out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
+                            "kv_commit": next_row_commit(r, torch, mean_us),
+                            "awl_loss": next_row_awl(r, torch, mean_us),
+                            "train_attn": next_row_train_attn(r, torch, mean_us)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
