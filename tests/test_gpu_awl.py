@@ -100,6 +100,22 @@ def test_awl_nothing_included_and_identical_models():
     _check(out, want, "f32", 15, inc_mask=x["include"])
 
 
+def test_awl_masked_vocabulary():
+    """Logits at -inf (a masked vocabulary tail) take no probability: they add nothing to either
+    softmax and get a zero gradient."""
+    require_gpu()
+    _say("awl_loss: masked vocabulary")
+    x = synth.awl_inputs(3, 15, 1024, dtype="f32", seed=12)
+    x["z_target"][..., 700:] = -np.inf
+    x["z_draft"][..., 700:] = -np.inf
+    x["tokens"] %= 700
+    x["labels"] %= 700
+    out = _run(x, "f32")
+    want = o_awl.awl_loss(x["z_target"], x["z_draft"], x["tokens"], x["labels"], x["include"])
+    _check(out, want, "f32", 15, inc_mask=x["include"])
+    assert not torch.any(out["grad"][..., 700:] != 0)
+
+
 def test_awl_training_step_shape_sampled():
     """128 anchor blocks x 15 future positions x 151936 (one training sample at B = 16): every weight,
     CE and the loss against the oracle block by block, the gradient on sampled rows."""

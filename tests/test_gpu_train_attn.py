@@ -83,6 +83,27 @@ def test_train_attention_parity(case):
         assert ok, (name, e, f)
 
 
+def test_train_attention_clamps_anchors():
+    """Anchors outside [0, L] are clamped (an empty prefix, the whole response): the result equals
+    the oracle's on the clamped anchors."""
+    require_gpu()
+    L, nb, B, hq, hkv = 96, 4, 16, 8, 2
+    _say("train_attn: anchors outside [0, L]")
+    q, k, v, do, _ = _problem(L, nb, B, hq, hkv, "sorted", seed=17)
+    raw = np.array([-5, 40, L + 30, 10**6], dtype=np.int32)
+    clamped = np.clip(raw, 0, L)
+    scale = 128 ** -0.5
+    qd, kd, vd, dod = (dev(x, "bf16") for x in (q, k, v, do))
+    an = torch.from_numpy(raw).cuda()
+    out, lse = _binding.train_attn_fwd(qd, kd, vd, an, L, B, scale=scale)
+    dq, dk, dv = _binding.train_attn_bwd(qd, kd, vd, out, dod, lse, an, L, B, scale=scale)
+    torch.cuda.synchronize()
+    want_o, _ = ta.forward(q, k, v, L, clamped, B, scale)
+    assert _close(host(out), want_o, 2e-2, 1e-2)[0]
+    for got, want in zip((dq, dk, dv), ta.backward(q, k, v, do, L, clamped, B, scale)):
+        assert _close(host(got), want)[0]
+
+
 def test_train_attention_training_step_shape_sampled():
     """One training sample at B = 16: a 4096-token response with 128 anchors, 32 query / 8 key-value
     heads. Sampled rows of o, lse and dq against the oracle row by row; dk and dv on keys whose
