@@ -95,54 +95,6 @@ __device__ __forceinline__ float block_max(float v, float *sh) {
   return r;
 }
 
-// Streams the nvec 16-byte vectors of a slice through f(vector, index), thread t taking vectors
-// t, t + 256, ... The full steps (U vectors for every lane) run with a uniform trip count and no
-// per-lane predicate, in two register sets used in turn: the next step's loads are issued before the
-// current step's vectors are consumed, so every wave keeps loads in flight while it computes (two
-// sets rather than a copy, which would wait for the loads). The logits are read once per pass:
-// non-temporal loads (with the gradient's non-temporal stores, about 8% faster for the whole call
-// than cached accesses when calls run back to back). A prefetch past the full steps reads
-// clamped, in-bounds positions and is not consumed; the remaining vectors follow one per lane.
-template <int U, typename F, typename P>
-__device__ __forceinline__ void stream_vecs(const u32x4 *vp, int nvec, F &&f, P &&after_first_loads) {
-  constexpr int S = kThreads * U;
-  const int full = nvec / S;
-  const int t = threadIdx.x;
-  const auto fetch = [&](u32x4 (&b)[U], int v0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) b[u] = __builtin_nontemporal_load(vp + min(v0 + u * kThreads, nvec - 1));
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the consumption that follows
-  };
-  const auto consume = [&](const u32x4 (&b)[U], int v0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) f(b[u], v0 + u * kThreads);
-  };
-  if (nvec <= 0) {
-    after_first_loads();
-    return;
-  }
-  u32x4 a[U], b[U];
-  fetch(a, t);
-  after_first_loads();
-  if (full > 0) {
-    int s = 0;
-    for (; s + 2 <= full; s += 2) {
-      fetch(b, t + (s + 1) * S);
-      consume(a, t + s * S);
-      fetch(a, t + (s + 2) * S);
-      consume(b, t + (s + 1) * S);
-    }
-    if (s < full) consume(a, t + s * S);
-  }
-  for (int v = full * S + t; v < nvec; v += kThreads) f(vp[v], v);
-}
-
-// Per-thread sum of 2^(z c - mc), c = log2(e) in fp32, mc = fl(m c) for a reference logit m: one fma
-// and one exp per element. The reference moves up only when a group's fp32 sum leaves the range (a
-// logit far above it, or the first finite logit: m starts at -inf and the first sum is not finite),
-// so every term stays below 2^120. As mc is a rounded product, the terms are exp(z - r) for
-// r = mc / c = m - rho / c with rho = m c - mc, which an fma gives exactly; the merge uses r, so the
-// rounding of mc costs no accuracy.
 // s 2^(mc - nmc), out of line: it runs only when the reference moves, and inlined, its constants
 // would hold registers for the whole streaming loop
 __device__ __attribute__((noinline)) double rescale(double s, float mc, float nmc) {
@@ -205,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void awl_stats_kernel(const AwlArgs a) {
     constexpr int W = 16 / sizeof(T);
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(base + begin);
     const int nvec = (end - begin) / W;
-    stream_vecs<4>(
+    stream_vecs<kThreads, 4>(
         vp, nvec,
         [&](const u32x4 &w, int) {
           float z[W];
@@ -361,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void awl_grad_kernel(const AwlArgs a) {
     u32x4 *wp = reinterpret_cast<u32x4 *>(dst + begin);
     const int nvec = (end - begin) / W;  // chunks hold whole vectors on this path
     const int lab_v = lab >= begin && lab < end ? (lab - begin) / W : -1;
-    stream_vecs<4>(
+    stream_vecs<kThreads, 4>(
         vp, nvec,
         [&](const u32x4 &w, int v) {
           float z[W];
@@ -377,6 +329,8 @@ __global__ __launch_bounds__(kThreads) void awl_grad_kernel(const AwlArgs a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(g[k]);
           }
+          // non-temporal, like the loads: the gradient is not read back here (about 8 % faster for
+          // the whole call than cached accesses when calls run back to back)
           __builtin_nontemporal_store(o, wp + v);
         },
         setup);

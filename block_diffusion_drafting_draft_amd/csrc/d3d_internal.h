@@ -122,6 +122,53 @@ __device__ __forceinline__ int match_request(const d3d_block_desc *descs, int b0
   return -1;
 }
 
+// Streams the nvec 16-byte vectors of a slice through f(vector, index) with NT threads, thread t
+// taking vectors t, t + NT, ... The full steps (U vectors for every lane) run with a uniform trip count and no
+// per-lane predicate, in two register sets used in turn: the next step's loads are issued before the
+// current step's vectors are consumed, so every wave keeps loads in flight while it computes (two
+// sets rather than a copy, which would wait for the loads). The data are read once per pass:
+// non-temporal loads. A prefetch past the full steps reads
+// clamped, in-bounds positions and is not consumed; the remaining vectors follow one per lane.
+template <int NT, int U, typename F, typename P>
+__device__ __forceinline__ void stream_vecs(const u32x4 *vp, int nvec, F &&f, P &&after_first_loads) {
+  constexpr int S = NT * U;
+  const int full = nvec / S;
+  const int t = threadIdx.x;
+  const auto fetch = [&](u32x4 (&b)[U], int v0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) b[u] = __builtin_nontemporal_load(vp + min(v0 + u * NT, nvec - 1));
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the consumption that follows
+  };
+  const auto consume = [&](const u32x4 (&b)[U], int v0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) f(b[u], v0 + u * NT);
+  };
+  if (nvec <= 0) {
+    after_first_loads();
+    return;
+  }
+  u32x4 a[U], b[U];
+  fetch(a, t);
+  after_first_loads();
+  if (full > 0) {
+    int s = 0;
+    for (; s + 2 <= full; s += 2) {
+      fetch(b, t + (s + 1) * S);
+      consume(a, t + s * S);
+      fetch(a, t + (s + 2) * S);
+      consume(b, t + (s + 1) * S);
+    }
+    if (s < full) consume(a, t + s * S);
+  }
+  for (int v = full * S + t; v < nvec; v += NT) f(vp[v], v);
+}
+
+// Per-thread sum of 2^(z c - mc), c = log2(e) in fp32, mc = fl(m c) for a reference logit m: one fma
+// and one exp per element. The reference moves up only when a group's fp32 sum leaves the range (a
+// logit far above it, or the first finite logit: m starts at -inf and the first sum is not finite),
+// so every term stays below 2^120. As mc is a rounded product, the terms are exp(z - r) for
+// r = mc / c = m - rho / c with rho = m c - mc, which an fma gives exactly; the merge uses r, so the
+// rounding of mc costs no accuracy.
 inline int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? D3D_OK : D3D_EHIP;
