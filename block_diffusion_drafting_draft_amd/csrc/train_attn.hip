@@ -84,19 +84,14 @@ __device__ __forceinline__ RowSeg row_seg(const TrainArgs &a, int pos) {
 
 // Workgroup id -> (item, kv head): the key / value head varies fastest, so with H_kv = 8 every item
 // of one head runs on one XCD (workgroup w runs on XCD w % 8) and its L2 holds that head's keys.
-// Items are taken in decreasing order: the last positions (blocks, then the end of the response)
-// have the longest walks and start first.
+// Items are taken from the end of the packed sequence: the block region first, then the response
+// from its end down, so the longer response walks start before the shorter ones.
 __device__ __forceinline__ void item_of(int n_items, int Hkv, int &item, int &g) {
   const int w = blockIdx.x;
   g = w % Hkv;
   item = n_items - 1 - w / Hkv;
 }
 
-template <typename F>
-__device__ __forceinline__ float wave_reduce(float v, F op) {
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
-  return v;
-}
 __device__ __forceinline__ int wave_min(int v) {
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
   return v;
