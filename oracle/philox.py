@@ -26,6 +26,7 @@ PHILOX_W64 = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
 
 PURPOSE_ACCEPT = 0
 PURPOSE_SAMPLE = 1
+PURPOSE_DRAFT = 2
 
 
 def philox4(counter, key, bits=32, rounds=10):
@@ -90,3 +91,9 @@ def uniforms(seed, position, request, round_, purpose):
     x0, x1, _, _ = philox4x32_10(position, request, round_, purpose,
                                  seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
     return uniform53(x0, x1)
+
+
+def uniform24(word):
+    """Map a 32-bit word to the open interval (0, 1) on a 24-bit grid: ((w >> 8) + 1/2) / 2^24 (exact
+    in binary32 and in binary64; never 0 or 1)."""
+    return ((np.asarray(word, dtype=np.uint64) >> np.uint64(8)).astype(np.float64) + 0.5) * (2.0 ** -24)

@@ -14,11 +14,18 @@ are chosen; the readings (listed in the design doc, R3 and R17):
   replacement. The full-accept anchor is the most likely token of the position after the block.
 * Order: larger logit first, ties to the lower token id (softmax at any temperature is monotone in
   the logit, so this is the order of the probabilities). NaN logits count as -inf.
+* Sampled drafting at temperature T > 0 (R21; [DScout] 实验结果 reports temperature-1 decoding):
+  the token of a row is a draw from softmax(z / T), taken by the Gumbel-max rule: the token with the
+  largest z_v / T + G_v, G_v = -ln(-ln u_v), ties to the lower id. The uniforms are counter-based so
+  that both sides draw the same ones: u_v = ((w >> 8) + 1/2) / 2^24 with w word (v mod 4) of
+  Philox4x32-10 at counter (v div 4, row index, round, 2) under the 64-bit seed.
 
 TEST INFRASTRUCTURE: see the package docstring.
 """
 
 import numpy as np
+
+from . import philox
 
 
 def topk(row, k, exclude=-1):
@@ -41,3 +48,25 @@ def alt_anchors(z_draft, tokens, z_next, coverage, fanout):
         out.extend(int(t) for t in topk(z_draft[k - 1], fanout, exclude=int(tokens[k - 1])))
     out.append(int(topk(z_next, 1)[0]))
     return np.array(out, dtype=np.int64)
+
+
+def gumbel_scores(row, temperature, seed, round_, row_index):
+    """z_v / T + G_v for every token of one row (float64; NaN logits count as -inf)."""
+    z = np.asarray(row, dtype=np.float64)
+    z = np.where(np.isnan(z), -np.inf, z)
+    v = np.arange(z.size, dtype=np.uint64)
+    seed = int(seed)
+    words = philox.philox4x32_10(v >> np.uint64(2), int(row_index), int(round_), philox.PURPOSE_DRAFT,
+                                 seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    w = np.choose((v & np.uint64(3)).astype(np.int64), words)
+    u = philox.uniform24(w)
+    return z / float(temperature) - np.log(-np.log(u))
+
+
+def sample_token(row, temperature, seed, round_, row_index):
+    """The sampled token of one row at temperature T > 0 (Gumbel-max; ties to the lower id), or -1
+    when every logit is -inf."""
+    s = gumbel_scores(row, temperature, seed, round_, row_index)
+    if not np.isfinite(s).any() and not (s == np.inf).any():
+        return -1
+    return int(np.argmax(s))

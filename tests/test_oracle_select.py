@@ -66,3 +66,33 @@ def test_anchor_is_never_the_rejected_draft_and_replacements_come_from_outside_i
             rejectable += 1
             assert verify.residual_mass(zt[k - 1], zd[k - 1], 1.0)[tok[k - 1]] == 0.0
     assert rejectable > 0
+
+
+def test_sampled_drafting_follows_the_softmax():
+    """Gumbel-max over the counter-based uniforms draws from softmax(z / T): the token frequencies
+    over 40000 rows (row indexes 0..39999) match the probabilities (chi-square, 5 cells)."""
+    from oracle import select as sel
+    z = np.array([1.0, 0.2, -0.5, 2.0, 0.0])
+    T = 0.8
+    p = np.exp(z / T) / np.exp(z / T).sum()
+    n = 40000
+    counts = np.bincount([sel.sample_token(z, T, 0x5EED, 3, r) for r in range(n)], minlength=5)
+    chi2 = float(((counts - n * p) ** 2 / (n * p)).sum())
+    assert chi2 < 20.5  # 4 degrees of freedom: p < 0.0004 under the right law
+
+
+def test_sampled_drafting_special_cases():
+    from oracle import select as sel
+    from oracle import philox
+    # the uniform map stays inside (0, 1) at the extreme words
+    assert 0.0 < float(philox.uniform24(0)) and float(philox.uniform24(0xFFFFFFFF)) < 1.0
+    # a very low temperature gives the argmax; -inf and NaN logits are never drawn
+    z = np.array([0.1, 3.0, 2.9, -np.inf, np.nan])
+    assert all(sel.sample_token(z, 1e-4, 7, 0, r) == 1 for r in range(50))
+    draws = {sel.sample_token(z, 5.0, 7, 0, r) for r in range(300)}
+    assert draws <= {0, 1, 2} and len(draws) == 3
+    # the same counter draws the same token; another row index draws independently
+    assert sel.sample_token(z, 1.0, 9, 4, 11) == sel.sample_token(z, 1.0, 9, 4, 11)
+    # the scores are z / T plus a standard Gumbel variable: mean Euler's constant over many tokens
+    g = sel.gumbel_scores(np.zeros(200000), 1.0, 1, 0, 0)
+    assert abs(g.mean() - 0.5772156649) < 0.01 and abs(g.var() - np.pi ** 2 / 6) < 0.03
