@@ -51,6 +51,7 @@ def parse():
                    help="skip the next-row measurements (token selection, KV commit, AWL, training attention)")
     p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss",
                                      "train_attn_fwd", "train_attn_bwd", "draft_topk_tokens", "draft_topk_anchors",
+                                     "draft_sample_tokens",
                                      "kv_commit"),
                    default=None,
                    help="only replay this call's graph (warmup + steps times, nothing else on the GPU) and print "
@@ -284,12 +285,13 @@ def main():
     if args.call:
         if args.call == "awl_loss":
             g = awl_graph(r, torch)[0]
-        elif args.call in ("draft_topk_tokens", "draft_topk_anchors"):
+        elif args.call in ("draft_topk_tokens", "draft_topk_anchors", "draft_sample_tokens"):
             tg = topk_graphs(r, torch)
             if tg is None:
                 print("this workload drafts no branches", file=sys.stderr)
                 return 2
-            g = tg[args.call.rsplit("_", 1)[1]][0]
+            g = tg[{"draft_topk_tokens": "tokens", "draft_topk_anchors": "anchors",
+                    "draft_sample_tokens": "sampled"}[args.call]][0]
         elif args.call == "kv_commit":
             g = next_row_commit(r, torch, None, graph_only=True)
         elif args.call in ("train_attn_fwd", "train_attn_bwd"):
@@ -596,8 +598,9 @@ def topk_graphs(r, torch):
     """Graphs of drafter token selection: greedy tokens of every masked position of the packed blocks
     (k = 1 over rows of drafter logits; synthetic N(0, 3) bf16 logits drawn on the device: timing
     only) and the branch anchors in the builder's layout (top-F of draft rows 1..C-1 excluding the
-    drafts, then the full-accept anchor). Returns {"tokens" | "anchors": (graph, rows read)}, or None
-    for workloads without branches."""
+    drafts, then the full-accept anchor), and the sampled tokens of the same masked positions at
+    temperature 1 (draft_sample). Returns {"tokens" | "anchors" | "sampled": (graph, rows read)}, or
+    None for workloads without branches."""
     w, lib = r.w, r.lib
     if not w.coverage or w.dtype != "bf16":
         return None
@@ -621,28 +624,36 @@ def topk_graphs(r, torch):
     ws_a = torch.empty(max(lib.draft_topk_workspace(rows.numel(), V, F), lib.draft_topk_workspace(n_req, V, 1)),
                        dtype=torch.uint8, device="cuda")
 
+    toks_s = torch.empty(masked.numel(), dtype=torch.int32, device="cuda")
+    ws_s = torch.empty(lib.draft_sample_workspace(masked.numel(), V), dtype=torch.uint8, device="cuda")
+
     def tokens():
         lib.draft_topk(logits, 1, rows=masked, out=toks, ws=ws_t)
+
+    def sampled():
+        lib.draft_sample(logits, 1.0, 0xD3D0 + w.seed, 0, rows=masked, out=toks_s, ws=ws_s)
 
     def anchors():
         lib.draft_topk(zd_rows, F, rows=rows, exclude=excl, out=alt, out_off=offs, ws=ws_a)
         lib.draft_topk(z_next, 1, out=alt, out_off=offs_full, ws=ws_a)
 
     out = {}
-    for name, fn, n_rows in (("tokens", tokens, masked.numel()), ("anchors", anchors, rows.numel() + n_req)):
+    for name, fn, n_rows in (("tokens", tokens, masked.numel()), ("anchors", anchors, rows.numel() + n_req),
+                             ("sampled", sampled, masked.numel())):
         fn()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
-        g.keep = (logits, masked, toks, rows, excl, offs, offs_full, z_next, alt, ws_t, ws_a)
+        g.keep = (logits, masked, toks, rows, excl, offs, offs_full, z_next, alt, ws_t, ws_a, toks_s, ws_s)
         out[name] = (g, int(n_rows))
     return out
 
 
 def next_row_topk(r, torch, cur, mean_us):
     """Drafter token selection (the first next row, not part of the step), timed as the mean of
-    back-to-back graph replays. HBM bytes = rows x V x 2."""
+    back-to-back graph replays. HBM bytes = rows x V x 2. The sampled tokens are ALU-bound (a Philox
+    block per 4 tokens and two logarithms per token): also reported in tokens scored per second."""
     graphs = topk_graphs(r, torch)
     if graphs is None:
         return None
@@ -653,6 +664,8 @@ def next_row_topk(r, torch, cur, mean_us):
         nbytes = n_rows * V * 2
         res[name] = {"rows": int(n_rows), "us": round(t, 3), "gbs": round(nbytes / (t * 1e-6) / 1e9, 1),
                      "pct_hbm_peak": round(100 * nbytes / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        if name == "sampled":
+            res[name]["gtokens_per_s"] = round(n_rows * V / (t * 1e-6) / 1e9, 1)
     return res
 
 

@@ -53,6 +53,9 @@ _SIGNATURES = {
     "draft_topk_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
     "draft_topk": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int,
                               _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "draft_sample_workspace": (_c.c_size_t, [_c.c_int, _c.c_int]),
+    "draft_sample": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p, _c.c_float, _c.c_uint64,
+                                _c.c_uint32, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "kv_commit": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
                              _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int,
                              _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
@@ -345,6 +348,36 @@ def draft_topk(logits, k, rows=None, exclude=None, out=None, out_off=None, n_row
     st = load().draft_topk(dt, _ptr(logits), vocab, n_rows, _ptr(rows), _ptr(exclude), k, _ptr(out), _ptr(out_off),
                            _ptr(ws), need, _stream(stream))
     _check(st, "draft_topk")
+    return out
+
+
+def draft_sample_workspace(n_rows, vocab):
+    return int(load().draft_sample_workspace(n_rows, vocab))
+
+
+def draft_sample(logits, temperature, seed, round_, rows=None, out=None, n_rows=None, ws=None, stream=None):
+    """One token per logit row drawn from softmax(z / T) (Gumbel-max over Philox uniforms, decided in
+    fp64). logits [rows_in, V] on the GPU; rows: int32 GPU tensor or None. Returns out (int32 [n_rows])."""
+    _dev(logits, "logits")
+    dt = _dtype_code(logits)
+    vocab = logits.shape[-1]
+    if rows is not None:
+        _dev(rows, "rows")
+        if rows.dtype != torch.int32:
+            raise TypeError("rows must be int32")
+    if n_rows is None:
+        n_rows = rows.numel() if rows is not None else logits.numel() // vocab
+    if out is None:
+        out = torch.empty(n_rows, dtype=torch.int32, device=logits.device)
+    _dev(out, "out")
+    need = draft_sample_workspace(n_rows, vocab)
+    if need == 0:
+        raise ValueError("unsupported draft_sample shape")
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    st = load().draft_sample(dt, _ptr(logits), vocab, n_rows, _ptr(rows), float(temperature), int(seed),
+                             int(round_) & 0xFFFFFFFF, _ptr(out), _ptr(ws), need, _stream(stream))
+    _check(st, "draft_sample")
     return out
 
 

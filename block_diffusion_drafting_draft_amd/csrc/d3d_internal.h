@@ -39,15 +39,26 @@ struct Philox4 {
   uint32_t x[4];
 };
 
+// a ^ b ^ k in one VALU instruction (the compiler emits two v_xor_b32 for it), k from a scalar
+// register: k must be wave-uniform.
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_xor3_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// The key (k0, k1) must be wave-uniform: every caller passes the seed from its kernel arguments.
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1) {
   constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
   constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t hi_a = __umulhi(kMulA, c0), lo_a = kMulA * c0;
-    const uint32_t hi_b = __umulhi(kMulB, c2), lo_b = kMulB * c2;
-    const uint32_t n0 = hi_b ^ c1 ^ k0, n2 = hi_a ^ c3 ^ k1;
+    // one 32 x 32 -> 64-bit product per word (v_mad_u64_u32) instead of separate high and low halves
+    const uint64_t pa = static_cast<uint64_t>(kMulA) * c0, pb = static_cast<uint64_t>(kMulB) * c2;
+    const uint32_t hi_a = static_cast<uint32_t>(pa >> 32), lo_a = static_cast<uint32_t>(pa);
+    const uint32_t hi_b = static_cast<uint32_t>(pb >> 32), lo_b = static_cast<uint32_t>(pb);
+    const uint32_t n0 = xor3_key(hi_b, c1, k0), n2 = xor3_key(hi_a, c3, k1);
     c0 = n0;
     c1 = lo_b;
     c2 = n2;
@@ -163,12 +174,6 @@ __device__ __forceinline__ void stream_vecs(const u32x4 *vp, int nvec, F &&f, P 
   for (int v = full * S + t; v < nvec; v += NT) f(vp[v], v);
 }
 
-// Per-thread sum of 2^(z c - mc), c = log2(e) in fp32, mc = fl(m c) for a reference logit m: one fma
-// and one exp per element. The reference moves up only when a group's fp32 sum leaves the range (a
-// logit far above it, or the first finite logit: m starts at -inf and the first sum is not finite),
-// so every term stays below 2^120. As mc is a rounded product, the terms are exp(z - r) for
-// r = mc / c = m - rho / c with rho = m c - mc, which an fma gives exactly; the merge uses r, so the
-// rounding of mc costs no accuracy.
 inline int launch_status() {
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? D3D_OK : D3D_EHIP;

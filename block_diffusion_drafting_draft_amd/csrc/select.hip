@@ -15,6 +15,20 @@
 //                  heads of the threads' lists. Partial k-list per (row, chunk).
 //   2. topk_merge  one workgroup per row: the same rounds over the chunks' candidates (one per
 //                  thread); writes the k ids.
+//
+// Sampled drafting at temperature T > 0 ([DScout] 实验结果 decodes at temperature 1): the token of a
+// row is a draw from softmax(z / T), taken as the token with the largest score z_v / T + G_v where
+// G_v = -ln(-ln u_v) is Gumbel noise (the Gumbel-max rule), ties to the lower id. u_v is a 24-bit
+// uniform ((w >> 8) + 1/2) / 2^24 of word (v mod 4) of Philox4x32-10 at counter (v div 4, logits row,
+// round, 2) under the 64-bit seed, so that any implementation of the same generator draws the same
+// token. The winner is decided in fp64; a cheap fp32 score is a filter in front of it:
+//   1. sample_chunk  grid (chunk, row), ALU-bound (one Philox block per 4 tokens, two logs per
+//                    token): each thread keeps a running maximum of its fp32 scores and evaluates
+//                    the fp64 score of every token whose fp32 score comes within a margin of that
+//                    maximum (the margin exceeds twice the fp32 error, so the fp64 winner is always
+//                    evaluated); a vector of tokens whose largest logit cannot reach the running
+//                    maximum even with the largest possible Gumbel value (17.33) is skipped whole.
+//   2. sample_merge  one workgroup per row: the best (fp64 score, id) of the chunks.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -273,6 +287,272 @@ void launch_select(const SelArgs &a, hipStream_t stream) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Sampled drafting (Gumbel-max over counter-based uniforms)
+
+struct SampCand {
+  double s;    // fp64 score, -inf: nothing finite seen
+  int32_t id;  // INT_MAX: empty
+  int32_t pad;
+};
+
+struct SampArgs {
+  const void *logits;
+  const int32_t *rows;  // row r reads logits row rows[r] (NULL: row r); the row index is the counter word
+  int32_t *out;         // [n_rows]
+  int vocab, n_rows, chunks, chunk_len;
+  float inv_t;  // fl(1 / T): the filter's scale
+  double t;     // T: the fp64 score divides by it
+  uint32_t k0, k1, round;
+  SampCand *part;  // [n_rows][chunks]
+};
+
+constexpr float kGumbelCap = 17.5f;  // > -ln(-ln(1 - 2^-25)) = 17.33, the largest Gumbel value drawn
+
+// -ln u for u = (m + 1/2) / 2^24, m = w >> 8, in fp32 with relative error below 1e-6: close to 1 (where
+// u itself is not representable in fp32) the series -ln(1 - t) = t + t^2/2 + ... in the exact
+// complement t = (2^24 - 1 - m + 1/2) / 2^24 < 2^-4; elsewhere -ln of the rounded u (|ln u| > 0.064).
+__device__ __forceinline__ float neg_log_u32(uint32_t w) {
+  const uint32_t m = w >> 8;
+  const uint32_t n = 0xFFFFFFu - m;
+  // both forms, then a select: nearly every wavefront has lanes on both sides
+  const float t = (static_cast<float>(n) + 0.5f) * 0x1p-24f;
+  float p = 1.0f / 6.0f;
+  p = fmaf(p, t, 0.2f);
+  p = fmaf(p, t, 0.25f);
+  p = fmaf(p, t, 1.0f / 3.0f);
+  p = fmaf(p, t, 0.5f);
+  p = fmaf(p, t, 1.0f);
+  const float lg = -__logf((static_cast<float>(m) + 0.5f) * 0x1p-24f);
+  return n < (1u << 20) ? p * t : lg;
+}
+
+// Upper bound of the Gumbel value -ln(-ln u), u = (m + 1/2) / 2^24, from the exponent alone: -ln u
+// >= 1 - u = (n + 1/2) / 2^24 with n = 2^24 - 1 - m, so G <= 24 ln 2 - ln(n + 1/2); for n in
+// [2^(e-1), 2^e) (frexp exponent e; e = 0 for n = 0) that is at most (25 - e) ln 2.
+__device__ __forceinline__ float gumbel_bound(uint32_t w) {
+  const uint32_t n = 0xFFFFFFu - (w >> 8);
+  const int e = __builtin_amdgcn_frexp_expf(static_cast<float>(n));  // exact: n < 2^24
+  return static_cast<float>(25 - e) * 0.69314718f + 1e-6f;
+}
+
+// Filter margin: well above twice the fp32 score error (about 4e-6 + 2e-7 |score|).
+__device__ __forceinline__ float samp_margin(float s) { return 1e-4f + 1e-6f * fabsf(s); }
+
+// fp32 filter score of one token (z already cleaned: NaN -> -inf).
+__device__ __forceinline__ float score32(const SampArgs &a, float z, uint32_t w) {
+  return fmaf(z, a.inv_t, -__logf(neg_log_u32(w)));
+}
+
+// fp64 score: z / T - ln(-ln u) with the exact uniform; this decides the token. Out of line: it
+// runs for one token per thread and for the rare ambiguous re-walk.
+__device__ __noinline__ double score64(const SampArgs &a, float z, uint32_t w) {
+  const double u = (static_cast<double>(w >> 8) + 0.5) * 0x1p-24;
+  return static_cast<double>(z) / a.t - log(-log(u));
+}
+
+__device__ __forceinline__ bool samp_better(double s, int id, double bs, int bi) {
+  return id != INT_MAX && (bi == INT_MAX || s > bs || (s == bs && id < bi));
+}
+
+// A thread's two best fp32 scores and the token of the best. When the second lies more than the margin
+// below the best, no other token of the thread can have a higher fp64 score than the best token (each
+// fp32 score is within half the margin of the fp64 one); otherwise the thread is ambiguous and
+// re-walks its tokens in fp64.
+struct SampTop2 {
+  float s1, s2, z1;
+  int id1;
+  uint32_t w1;
+  __device__ __forceinline__ void init() {
+    s1 = -INFINITY;
+    s2 = -INFINITY;
+    z1 = -INFINITY;
+    id1 = INT_MAX;
+    w1 = 0;
+  }
+  __device__ __forceinline__ void push(float s, float z, int id, uint32_t w) {
+    if (s > s1 || id1 == INT_MAX) {  // ids grow within a thread: an equal score lands in s2
+      s2 = s1;
+      s1 = s;
+      z1 = z;
+      id1 = id;
+      w1 = w;
+    } else {
+      s2 = fmaxf(s2, s);
+    }
+  }
+};
+
+// Visits the thread's tokens of one chunk: f(z, id, word) for every token, or, where a whole
+// 16-byte vector's largest logit cannot reach `floor(s)` even with the largest Gumbel value, none of
+// the vector (its noise is not generated). floor() is re-read per vector: it may rise as tokens pass.
+template <typename T, bool VEC, typename F, typename FLOOR>
+__device__ __forceinline__ void samp_walk(const SampArgs &a, const T *base, int begin, int end, uint32_t ctr_row,
+                                          F &&f, FLOOR &&floor_of) {
+  if constexpr (VEC) {
+    constexpr int W = 16 / sizeof(T);  // tokens per vector: 8 (bf16) or 4 (fp32), W-aligned ids
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(base + begin);
+    const int nvec = (end - begin) / W;
+    constexpr int U = 4;
+    for (int v0 = threadIdx.x; v0 < nvec; v0 += kThreads * U) {
+      u32x4 buf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) buf[u] = vp[min(v0 + u * kThreads, nvec - 1)];  // clamped, in bounds
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * kThreads;
+        if (v < nvec) {
+          float z[W];
+          unpack_w<T, W>(buf[u], z);
+          float zmax = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < W; ++e) {
+            z[e] = clean(z[e]);
+            zmax = fmaxf(zmax, z[e]);
+          }
+          if (fmaf(zmax, a.inv_t, kGumbelCap) < floor_of()) continue;
+          const int id0 = begin + v * W;
+#pragma unroll
+          for (int q = 0; q < W / 4; ++q) {
+            const Philox4 ph = philox4x32_10(static_cast<uint32_t>(id0 / 4 + q), ctr_row, a.round, 2u, a.k0, a.k1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f(z[4 * q + e], id0 + 4 * q + e, ph.x[e]);
+          }
+        }
+      }
+    }
+  } else {
+    // scalar path: each thread takes the 4 consecutive tokens of one Philox block at a time
+    for (int t0 = (begin & ~3) + 4 * static_cast<int>(threadIdx.x); t0 < end; t0 += 4 * kThreads) {
+      const Philox4 ph = philox4x32_10(static_cast<uint32_t>(t0 / 4), ctr_row, a.round, 2u, a.k0, a.k1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + e;
+        if (t >= begin && t < end) f(clean(load_elem(base + t)), t, ph.x[e]);
+      }
+    }
+  }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_chunk_kernel(const SampArgs a) {
+  __shared__ double sh_s[kThreads / 64];
+  __shared__ int sh_id[kThreads / 64];
+  const int r = blockIdx.y, chunk = blockIdx.x;
+  const int row = a.rows ? a.rows[r] : r;
+  const T *base = static_cast<const T *>(a.logits) + static_cast<size_t>(row) * a.vocab;
+  const int begin = chunk * a.chunk_len;
+  const int end = min(begin + a.chunk_len, a.vocab);
+  const uint32_t ctr_row = static_cast<uint32_t>(row);
+  SampTop2 t2;
+  t2.init();
+  samp_walk<T, VEC>(
+      a, base, begin, end, ctr_row,
+      [&](float z, int id, uint32_t w) {
+        // a token whose score bound stays below the second score changes neither score: its logs
+        // are skipped
+        if (fmaf(z, a.inv_t, gumbel_bound(w)) < t2.s2 - samp_margin(t2.s2)) return;
+        t2.push(score32(a, z, w), z, id, w);
+      },
+      [&] { return t2.s2 - samp_margin(t2.s2); });
+  // Both skip tests use the second score: a skipped token's fp32 score lies below it, so the token
+  // can neither be the best nor change the second score.
+  double bs = -INFINITY;
+  int bi = INT_MAX;
+  if (t2.id1 != INT_MAX && t2.s1 > -INFINITY) {
+    if (t2.s2 < t2.s1 - samp_margin(t2.s1)) {
+      bs = score64(a, t2.z1, t2.w1);
+      bi = t2.id1;
+    } else {
+      // ambiguous (rare): every token of the thread within the margin of the best, in fp64, one
+      // Philox block at a time (kept compact: this path is cold)
+      const float lim = t2.s1 - samp_margin(t2.s1);
+      const auto visit = [&](int t, uint32_t w) {
+        if (t < begin || t >= end) return;
+        const float z = clean(load_elem(base + t));
+        if (!(score32(a, z, w) < lim)) {  // NaN limit (an infinite best): every token
+          const double sd = score64(a, z, w);
+          if (samp_better(sd, t, bs, bi)) {
+            bs = sd;
+            bi = t;
+          }
+        }
+      };
+      // the same tokens as the main walk: whole W-token vectors v = tid, tid + NT, ... (vector path)
+      // or Philox blocks of 4 tokens (scalar path)
+      constexpr int W = VEC ? 16 / static_cast<int>(sizeof(T)) : 4;
+      const int first = VEC ? begin : (begin & ~3);
+#pragma unroll 1
+      for (int t0 = first + W * static_cast<int>(threadIdx.x); t0 < end; t0 += W * kThreads) {
+#pragma unroll 1
+        for (int q = 0; q < W / 4; ++q) {
+          const Philox4 ph = philox4x32_10(static_cast<uint32_t>(t0 / 4 + q), ctr_row, a.round, 2u, a.k0, a.k1);
+#pragma unroll 1
+          for (int e = 0; e < 4; ++e) visit(t0 + 4 * q + e, ph.x[e]);
+        }
+      }
+    }
+  }
+  // workgroup argmax of (fp64 score, id), ties to the lower id; an empty slot loses to everything
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    const double os = __shfl_xor(bs, o);
+    const int oi = __shfl_xor(bi, o);
+    if (samp_better(os, oi, bs, bi)) {
+      bs = os;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    sh_s[wave] = bs;
+    sh_id[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kThreads / 64; ++w) {
+      if (samp_better(sh_s[w], sh_id[w], bs, bi)) {
+        bs = sh_s[w];
+        bi = sh_id[w];
+      }
+    }
+    SampCand c;
+    c.s = bs;
+    c.id = bi;
+    c.pad = 0;
+    a.part[static_cast<size_t>(r) * a.chunks + chunk] = c;
+  }
+}
+
+// One wavefront per row: the best chunk candidate (chunks are in id order; ties to the lower id). A
+// row whose best score is -inf (every logit -inf or NaN) gets -1.
+__global__ __launch_bounds__(64) void sample_merge_kernel(const SampArgs a) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  double bs = -INFINITY;
+  int bi = INT_MAX;
+  for (int c = lane; c < a.chunks; c += 64) {
+    const SampCand x = a.part[static_cast<size_t>(r) * a.chunks + c];
+    if (samp_better(x.s, x.id, bs, bi)) {
+      bs = x.s;
+      bi = x.id;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const double os = __shfl_xor(bs, o);
+    const int oi = __shfl_xor(bi, o);
+    if (samp_better(os, oi, bs, bi)) {
+      bs = os;
+      bi = oi;
+    }
+  }
+  if (lane == 0) a.out[r] = bi == INT_MAX ? -1 : bi;
+}
+
+template <typename T, bool VEC>
+void launch_sample(const SampArgs &a, hipStream_t stream) {
+  sample_chunk_kernel<T, VEC><<<dim3(a.chunks, a.n_rows), kThreads, 0, stream>>>(a);
+  sample_merge_kernel<<<a.n_rows, 64, 0, stream>>>(a);
+}
+
 }  // namespace
 }  // namespace d3d
 
@@ -315,6 +595,53 @@ extern "C" int draft_topk(d3d_dtype dtype, const void *logits, int vocab, int n_
       launch_select<float, true>(a, stream);
     else
       launch_select<float, false>(a, stream);
+  }
+  return launch_status();
+}
+
+extern "C" size_t draft_sample_workspace(int n_rows, int vocab) {
+  d3d::SelPlan p;
+  if (d3d::plan_select(n_rows, vocab, 1, &p) != D3D_OK) return 0;
+  return d3d::align_up(sizeof(d3d::SampCand) * static_cast<size_t>(n_rows) * p.chunks, 256);
+}
+
+extern "C" int draft_sample(d3d_dtype dtype, const void *logits, int vocab, int n_rows, const int32_t *rows,
+                            float temperature, uint64_t seed, uint32_t round, int32_t *out, void *ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  using namespace d3d;
+  if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
+  if (!logits || !out) return D3D_EINVAL;
+  if (!(temperature > 0.0f) || !(temperature < INFINITY)) return D3D_EINVAL;
+  SelPlan p;
+  if (plan_select(n_rows, vocab, 1, &p) != D3D_OK) return D3D_EINVAL;
+  const size_t need = align_up(sizeof(SampCand) * static_cast<size_t>(n_rows) * p.chunks, 256);
+  if (!ws || ws_bytes < need) return D3D_EWORKSPACE;
+  SampArgs a;
+  a.logits = logits;
+  a.rows = rows;
+  a.out = out;
+  a.vocab = vocab;
+  a.n_rows = n_rows;
+  a.chunks = p.chunks;
+  a.chunk_len = p.chunk_len;
+  a.inv_t = 1.0f / temperature;
+  a.t = static_cast<double>(temperature);
+  a.k0 = static_cast<uint32_t>(seed);
+  a.k1 = static_cast<uint32_t>(seed >> 32);
+  a.round = round;
+  a.part = static_cast<SampCand *>(ws);
+  const size_t esize = dtype == D3D_BF16 ? 2 : 4;
+  const bool vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 && (static_cast<size_t>(vocab) * esize) % 16 == 0;
+  if (dtype == D3D_BF16) {
+    if (vec)
+      launch_sample<__bf16, true>(a, stream);
+    else
+      launch_sample<__bf16, false>(a, stream);
+  } else {
+    if (vec)
+      launch_sample<float, true>(a, stream);
+    else
+      launch_sample<float, false>(a, stream);
   }
   return launch_status();
 }

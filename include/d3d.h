@@ -238,6 +238,29 @@ int draft_topk(d3d_dtype dtype, const void *logits, int vocab, int n_rows, const
                size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Sampled drafting at temperature T > 0 ([D3D] 方法步骤详情 step 4: the packed forward drafts every
+ * masked position; [DScout] 实验结果 decodes at temperature 1): the token of each logit row is a draw
+ * from softmax(z / T), taken by the Gumbel-max rule as the token with the largest
+ * z_v / T - ln(-ln u_v), ties to the lower id, decided in fp64. u_v = ((w >> 8) + 1/2) / 2^24 with w
+ * word (v mod 4) of Philox4x32-10 (Salmon et al., SC'11) at counter (v div 4, logits row index,
+ * round, 2) under the key (seed low word, seed high word). NaN logits count as -inf; a row whose
+ * logits are all -inf gets -1. Greedy drafting (T = 0) is draft_topk with k = 1.
+ *
+ *  logits       [rows_in, vocab] (dtype), DEVICE; vocab >= 1
+ *  rows         [n_rows] DEVICE row indexes into logits, or NULL for rows 0..n_rows-1; the row index
+ *               (rows[r], or r) is the generator's second counter word
+ *  temperature  finite, > 0
+ *  out          [n_rows] DEVICE int32: the drawn token of each row
+ *  ws           at least draft_sample_workspace(n_rows, vocab) bytes; no initial contents required.
+ * Errors: D3D_EINVAL on bad sizes (n_rows < 1, vocab < 1), a temperature that is not finite and
+ * positive, or NULL pointers; D3D_EWORKSPACE if ws is too small. Row indexes are not range-checked.
+ * ------------------------------------------------------------------------------------------- */
+size_t draft_sample_workspace(int n_rows, int vocab);
+int draft_sample(d3d_dtype dtype, const void *logits, int vocab, int n_rows, const int32_t *rows,
+                 float temperature, uint64_t seed, uint32_t round, int32_t *out, void *ws, size_t ws_bytes,
+                 hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * KV commit of the accepted slice and promotion of the hit branch ([D3D] 前置知识: 异步起草与缓存命中,
  * 方法步骤详情 step 4). After verification request i's prefix grows by its anchor and accepted drafts:
  * rows 0..n_acc_i of its block 0 in the packed k_new / v_new (causal in-block, so they are prefix

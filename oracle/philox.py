@@ -95,5 +95,5 @@ def uniforms(seed, position, request, round_, purpose):
 
 def uniform24(word):
     """Map a 32-bit word to the open interval (0, 1) on a 24-bit grid: ((w >> 8) + 1/2) / 2^24 (exact
-    in binary32 and in binary64; never 0 or 1)."""
+    in binary64, which needs 25 significant bits here; never 0 or 1)."""
     return ((np.asarray(word, dtype=np.uint64) >> np.uint64(8)).astype(np.float64) + 0.5) * (2.0 ** -24)

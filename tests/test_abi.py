@@ -24,6 +24,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "draft_attn_packed", "draft_attn_packed_workspace",
                  "spec_verify", "spec_verify_workspace", "branch_cache_match", "draft_topk", "draft_topk_workspace",
+                 "draft_sample", "draft_sample_workspace",
                  "kv_commit", "awl_loss", "awl_loss_workspace", "train_attn_workspace", "train_attn_fwd",
                  "train_attn_bwd", "spec_verify_match", "draft_attn_packed_join", "d3d_status_string"):
         assert want in names
