@@ -39,15 +39,6 @@ struct Philox4 {
   uint32_t x[4];
 };
 
-// a ^ b ^ k in one VALU instruction (the compiler emits two v_xor_b32 for it), k from a scalar
-// register: k must be wave-uniform.
-__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_xor3_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
-}
-
-// The key (k0, k1) must be wave-uniform: every caller passes the seed from its kernel arguments.
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1) {
   constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
@@ -58,7 +49,7 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     const uint64_t pa = static_cast<uint64_t>(kMulA) * c0, pb = static_cast<uint64_t>(kMulB) * c2;
     const uint32_t hi_a = static_cast<uint32_t>(pa >> 32), lo_a = static_cast<uint32_t>(pa);
     const uint32_t hi_b = static_cast<uint32_t>(pb >> 32), lo_b = static_cast<uint32_t>(pb);
-    const uint32_t n0 = xor3_key(hi_b, c1, k0), n2 = xor3_key(hi_a, c3, k1);
+    const uint32_t n0 = hi_b ^ c1 ^ k0, n2 = hi_a ^ c3 ^ k1;
     c0 = n0;
     c1 = lo_b;
     c2 = n2;
