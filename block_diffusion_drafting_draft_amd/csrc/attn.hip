@@ -150,6 +150,20 @@ __device__ __forceinline__ LaneRow lane_row(const AttnArgs &a, const Item &it, i
   return L;
 }
 
+// The output row of query-head row `row` only (no descriptor read): what the final write needs.
+__device__ __forceinline__ LaneRow out_row(const AttnArgs &a, const Item &it, int row) {
+  const int head_local = row / a.Qt, qi = row - head_local * a.Qt;
+  LaneRow L;
+  L.q_local = it.tile * a.Qt + qi;
+  L.valid = L.q_local < it.R.n_q;
+  L.h = it.g * a.G + head_local;
+  L.blk = -1;
+  L.pos = 0;
+  L.r = 0;
+  L.causal = false;
+  return L;
+}
+
 // Per-wavefront online-softmax state for 32 query columns.
 template <int D>
 struct RowState {
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
                      [&](int kc) { return tail_visible(L, sh_blk + 4 * hh, sh_pos + 4 * hh, kc); });
     }
   }
-  write_result<__bf16, D>(a, it, row_of(), st.o, st.m, st.l);
+  write_result<__bf16, D>(a, it, out_row(a, it, wave * 32 + (lane & 31)), st.o, st.m, st.l);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -789,9 +803,12 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
       best_t = t;
     }
   }
-  // The first split also walks the in-pack tail (at most ceil((B + Qt) / 64) tiles), so it gets that
-  // many fewer prefix keys and every split carries about the same number of tiles.
-  const int tail_keys = (B + Qt + kKeys - 1) / kKeys * kKeys;
+  // The first split also walks the in-pack tail (at most ceil((B + Qt) / 64) tiles), so it gets fewer
+  // prefix keys and every split takes about the same time. A tail tile costs about 1.75 prefix tiles
+  // (measured per workgroup: its rows are gathered through per-key tables, its copy is not
+  // pipelined and its softmax is masked), so the first split gives up that many prefix keys per tail
+  // tile, rounded down to whole tiles of its own.
+  const int tail_keys = (B + Qt + kKeys - 1) / kKeys * kKeys * 7 / 4;
   for (int i = 0; i < n_req; ++i) {
     if (pre[i] == 0) {
       splits[i] = 1;
@@ -805,7 +822,7 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
       continue;
     }
     const int share = ((pre[i] + tail_keys + si - 1) / si + kKeys - 1) / kKeys * kKeys;
-    const int l0 = std::max(kKeys, std::min(pre[i], share - tail_keys));
+    const int l0 = std::max(kKeys, std::min(pre[i], (share - tail_keys) / kKeys * kKeys));
     const int rest = pre[i] - l0;
     if (rest <= 0) {
       splits[i] = 1;
