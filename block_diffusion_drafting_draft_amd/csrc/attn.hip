@@ -660,8 +660,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel_f32(const AttnArgs a)
 }
 
 // Merge split partials: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. Each thread owns four
-// consecutive elements of one row (16-byte loads); D/4 threads per row.
-template <typename T, int D>
+// consecutive elements of one row (16-byte loads); D/4 threads per row. MS bounds the split count
+// (its load arrays are unrolled to MS): 8 keeps the kernel near 60 registers, so the whole grid of a
+// 384-query pack is resident at once; 16 serves plans with more splits.
+template <typename T, int D, int MS>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
   constexpr int TPR = D / 4;  // threads per row
   const int row = blockIdx.x * (kThreads / TPR) + threadIdx.x / TPR;
@@ -679,10 +681,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
   const size_t slot0 = static_cast<size_t>(R.part_begin) + static_cast<size_t>(q_local) * a.Hq + h;
   // every partial is loaded up front (one round trip), then merged in split order
   const int ns = R.n_splits;
-  float pm[kMaxSplits], pl[kMaxSplits];
-  f32x4 po[kMaxSplits];
+  float pm[MS], pl[MS];
+  f32x4 po[MS];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < MS; ++s) {
     pm[s] = -INFINITY;
     pl[s] = 0.f;
     po[s] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -695,11 +697,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, pm[s]);
+  for (int s = 0; s < MS; ++s) M = fmaxf(M, pm[s]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < MS; ++s) {
     const float wgt = s < ns ? __builtin_amdgcn_exp2f(pm[s] - M) : 0.f;
     lsum += wgt * pl[s];
 #pragma unroll
@@ -729,6 +731,7 @@ struct AttnPlan {
   int comb_grid;
   size_t part_slots;
   size_t ws_bytes;
+  int max_splits;  // largest split count of any request
 };
 
 // Compute units of the current device (one bf16 / fp32 workgroup each); 256 when no device answers.
@@ -870,6 +873,8 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
     t_max = std::max(t_max, tiles[i]);
   }
   if (part >= (1ull << 31)) return D3D_EUNSUPPORTED;
+  P->max_splits = 1;
+  for (int i = 0; i < n_req; ++i) P->max_splits = std::max(P->max_splits, splits[i]);
   a.n_groups = groups;
   a.t_max = t_max;
   a.comb_rows = comb;
@@ -900,7 +905,12 @@ void launch(const AttnPlan &P, bool paged, hipEvent_t join, hipStream_t stream) 
     }
   }
   if (join) (void)hipStreamWaitEvent(stream, join, 0);  // the caller's other stream joins here
-  if (P.args.comb_rows > 0) combine_kernel<T, D><<<P.comb_grid, kThreads, 0, stream>>>(P.args);
+  if (P.args.comb_rows > 0) {
+    if (P.max_splits <= 8)
+      combine_kernel<T, D, 8><<<P.comb_grid, kThreads, 0, stream>>>(P.args);
+    else
+      combine_kernel<T, D, kMaxSplits><<<P.comb_grid, kThreads, 0, stream>>>(P.args);
+  }
 }
 
 }  // namespace
