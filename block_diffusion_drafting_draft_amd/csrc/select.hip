@@ -22,12 +22,13 @@
 // uniform ((w >> 8) + 1/2) / 2^24 of word (v mod 4) of Philox4x32-10 at counter (v div 4, logits row,
 // round, 2) under the 64-bit seed, so that any implementation of the same generator draws the same
 // token. The winner is decided in fp64; a cheap fp32 score is a filter in front of it:
-//   1. sample_chunk  grid (chunk, row), ALU-bound (one Philox block per 4 tokens, two logs per
-//                    token): each thread keeps a running maximum of its fp32 scores and evaluates
-//                    the fp64 score of every token whose fp32 score comes within a margin of that
-//                    maximum (the margin exceeds twice the fp32 error, so the fp64 winner is always
-//                    evaluated); a vector of tokens whose largest logit cannot reach the running
-//                    maximum even with the largest possible Gumbel value (17.33) is skipped whole.
+//   1. sample_chunk  grid (chunk, row), ALU-bound (one Philox block per 4 tokens, two base-2 logs
+//                    per token, no per-token branch): each thread keeps its two best fp32 scores;
+//                    when they lie more than a margin apart (the margin exceeds twice the fp32
+//                    error) the best token is the thread's fp64 winner and only its fp64 score is
+//                    computed, otherwise the thread re-scores its tokens within the margin in fp64.
+//                    A 16-byte vector of tokens whose largest logit cannot reach the thread's second
+//                    score even with the largest Gumbel value drawn (17.33) is skipped whole.
 //   2. sample_merge  one workgroup per row: the best (fp64 score, id) of the chunks.
 #include <float.h>
 #include <limits.h>
@@ -301,21 +302,24 @@ struct SampArgs {
   const int32_t *rows;  // row r reads logits row rows[r] (NULL: row r); the row index is the counter word
   int32_t *out;         // [n_rows]
   int vocab, n_rows, chunks, chunk_len;
-  float inv_t;  // fl(1 / T): the filter's scale
+  float c2;     // fl(log2(e) / T): the filter's scale
   double t;     // T: the fp64 score divides by it
   uint32_t k0, k1, round;
   SampCand *part;  // [n_rows][chunks]
 };
 
-constexpr float kGumbelCap = 17.5f;  // > -ln(-ln(1 - 2^-25)) = 17.33, the largest Gumbel value drawn
+// The fp32 filter works in log2 units: z log2(e) / T - log2(-log2 u) orders the tokens exactly as the
+// score z / T - ln(-ln u) does (a positive factor and a dropped constant, log2(ln 2)), and needs only
+// the hardware base-2 logarithm (every argument here is a normal float).
+constexpr float kGumbelCap2 = 25.5f;  // > 25.0, the largest Gumbel value drawn, in log2 units
 
-// -ln u for u = (m + 1/2) / 2^24, m = w >> 8, in fp32 with relative error below 1e-6: close to 1 (where
-// u itself is not representable in fp32) the series -ln(1 - t) = t + t^2/2 + ... in the exact
-// complement t = (2^24 - 1 - m + 1/2) / 2^24 < 2^-4; elsewhere -ln of the rounded u (|ln u| > 0.064).
-__device__ __forceinline__ float neg_log_u32(uint32_t w) {
+// -log2 u for u = (m + 1/2) / 2^24, m = w >> 8, in fp32 with relative error below 1e-6: close to 1
+// (where u itself is not representable in fp32) the series -log2(1 - t) = (t + t^2/2 + ...) / ln 2 in
+// the exact complement t = (2^24 - 1 - m + 1/2) / 2^24 < 2^-4; elsewhere -log2 of the rounded u
+// (|log2 u| > 0.093). Both forms, then a select: nearly every wavefront has lanes on both sides.
+__device__ __forceinline__ float neg_log2_u32(uint32_t w) {
   const uint32_t m = w >> 8;
   const uint32_t n = 0xFFFFFFu - m;
-  // both forms, then a select: nearly every wavefront has lanes on both sides
   const float t = (static_cast<float>(n) + 0.5f) * 0x1p-24f;
   float p = 1.0f / 6.0f;
   p = fmaf(p, t, 0.2f);
@@ -323,25 +327,16 @@ __device__ __forceinline__ float neg_log_u32(uint32_t w) {
   p = fmaf(p, t, 1.0f / 3.0f);
   p = fmaf(p, t, 0.5f);
   p = fmaf(p, t, 1.0f);
-  const float lg = -__logf((static_cast<float>(m) + 0.5f) * 0x1p-24f);
-  return n < (1u << 20) ? p * t : lg;
+  const float lg = -__builtin_amdgcn_logf((static_cast<float>(m) + 0.5f) * 0x1p-24f);
+  return n < (1u << 20) ? p * t * 1.44269504f : lg;
 }
 
-// Upper bound of the Gumbel value -ln(-ln u), u = (m + 1/2) / 2^24, from the exponent alone: -ln u
-// >= 1 - u = (n + 1/2) / 2^24 with n = 2^24 - 1 - m, so G <= 24 ln 2 - ln(n + 1/2); for n in
-// [2^(e-1), 2^e) (frexp exponent e; e = 0 for n = 0) that is at most (25 - e) ln 2.
-__device__ __forceinline__ float gumbel_bound(uint32_t w) {
-  const uint32_t n = 0xFFFFFFu - (w >> 8);
-  const int e = __builtin_amdgcn_frexp_expf(static_cast<float>(n));  // exact: n < 2^24
-  return static_cast<float>(25 - e) * 0.69314718f + 1e-6f;
-}
-
-// Filter margin: well above twice the fp32 score error (about 4e-6 + 2e-7 |score|).
+// Filter margin, in log2 units: well above twice the fp32 score error (about 6e-6 + 3e-7 |score|).
 __device__ __forceinline__ float samp_margin(float s) { return 1e-4f + 1e-6f * fabsf(s); }
 
-// fp32 filter score of one token (z already cleaned: NaN -> -inf).
+// fp32 filter score of one token (z already cleaned: NaN -> -inf), in log2 units.
 __device__ __forceinline__ float score32(const SampArgs &a, float z, uint32_t w) {
-  return fmaf(z, a.inv_t, -__logf(neg_log_u32(w)));
+  return fmaf(z, a.c2, -__builtin_amdgcn_logf(neg_log2_u32(w)));
 }
 
 // fp64 score: z / T - ln(-ln u) with the exact uniform; this decides the token. Out of line: it
@@ -355,37 +350,33 @@ __device__ __forceinline__ bool samp_better(double s, int id, double bs, int bi)
   return id != INT_MAX && (bi == INT_MAX || s > bs || (s == bs && id < bi));
 }
 
+// The Philox word of token t of a row (word t mod 4 of block t div 4).
+__device__ __forceinline__ uint32_t samp_word(const SampArgs &a, uint32_t ctr_row, int t) {
+  const Philox4 ph = philox4x32_10(static_cast<uint32_t>(t / 4), ctr_row, a.round, 2u, a.k0, a.k1);
+  const int e = t & 3;
+  return e == 0 ? ph.x[0] : e == 1 ? ph.x[1] : e == 2 ? ph.x[2] : ph.x[3];
+}
+
 // A thread's two best fp32 scores and the token of the best. When the second lies more than the margin
 // below the best, no other token of the thread can have a higher fp64 score than the best token (each
 // fp32 score is within half the margin of the fp64 one); otherwise the thread is ambiguous and
-// re-walks its tokens in fp64.
+// re-walks its tokens in fp64. Ids grow within a thread, so an equal score keeps the earlier token
+// and lands in s2 (ambiguous). No per-token branch: a max, a min and one select.
 struct SampTop2 {
-  float s1, s2, z1;
+  float s1, s2;
   int id1;
-  uint32_t w1;
   __device__ __forceinline__ void init() {
     s1 = -INFINITY;
     s2 = -INFINITY;
-    z1 = -INFINITY;
     id1 = INT_MAX;
-    w1 = 0;
   }
-  __device__ __forceinline__ void push(float s, float z, int id, uint32_t w) {
-    if (s > s1 || id1 == INT_MAX) {  // ids grow within a thread: an equal score lands in s2
-      s2 = s1;
-      s1 = s;
-      z1 = z;
-      id1 = id;
-      w1 = w;
-    } else {
-      s2 = fmaxf(s2, s);
-    }
+  __device__ __forceinline__ void push(float s, int id) {
+    id1 = s > s1 ? id : id1;
+    s2 = fmaxf(s2, fminf(s, s1));
+    s1 = fmaxf(s1, s);
   }
 };
 
-// Visits the thread's tokens of one chunk: f(z, id, word) for every token, or, where a whole
-// 16-byte vector's largest logit cannot reach `floor(s)` even with the largest Gumbel value, none of
-// the vector (its noise is not generated). floor() is re-read per vector: it may rise as tokens pass.
 template <typename T, bool VEC, typename F, typename FLOOR>
 __device__ __forceinline__ void samp_walk(const SampArgs &a, const T *base, int begin, int end, uint32_t ctr_row,
                                           F &&f, FLOOR &&floor_of) {
@@ -410,7 +401,7 @@ __device__ __forceinline__ void samp_walk(const SampArgs &a, const T *base, int 
             z[e] = clean(z[e]);
             zmax = fmaxf(zmax, z[e]);
           }
-          if (fmaf(zmax, a.inv_t, kGumbelCap) < floor_of()) continue;
+          if (fmaf(zmax, a.c2, kGumbelCap2) < floor_of()) continue;
           const int id0 = begin + v * W;
 #pragma unroll
           for (int q = 0; q < W / 4; ++q) {
@@ -447,22 +438,17 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(const SampArgs a
   SampTop2 t2;
   t2.init();
   samp_walk<T, VEC>(
-      a, base, begin, end, ctr_row,
-      [&](float z, int id, uint32_t w) {
-        // a token whose score bound stays below the second score changes neither score: its logs
-        // are skipped
-        if (fmaf(z, a.inv_t, gumbel_bound(w)) < t2.s2 - samp_margin(t2.s2)) return;
-        t2.push(score32(a, z, w), z, id, w);
-      },
+      a, base, begin, end, ctr_row, [&](float z, int id, uint32_t w) { t2.push(score32(a, z, w), id); },
       [&] { return t2.s2 - samp_margin(t2.s2); });
-  // Both skip tests use the second score: a skipped token's fp32 score lies below it, so the token
-  // can neither be the best nor change the second score.
+  // The skip test uses the second score: a skipped vector's fp32 scores lie below it, so none of its
+  // tokens can be the best or change the second score.
   double bs = -INFINITY;
   int bi = INT_MAX;
   if (t2.id1 != INT_MAX && t2.s1 > -INFINITY) {
     if (t2.s2 < t2.s1 - samp_margin(t2.s1)) {
-      bs = score64(a, t2.z1, t2.w1);
-      bi = t2.id1;
+      const int t = t2.id1;
+      bs = score64(a, clean(load_elem(base + t)), samp_word(a, ctr_row, t));
+      bi = t;
     } else {
       // ambiguous (rare): every token of the thread within the margin of the best, in fp64, one
       // Philox block at a time (kept compact: this path is cold)
@@ -624,7 +610,7 @@ extern "C" int draft_sample(d3d_dtype dtype, const void *logits, int vocab, int 
   a.n_rows = n_rows;
   a.chunks = p.chunks;
   a.chunk_len = p.chunk_len;
-  a.inv_t = 1.0f / temperature;
+  a.c2 = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
   a.t = static_cast<double>(temperature);
   a.k0 = static_cast<uint32_t>(seed);
   a.k1 = static_cast<uint32_t>(seed >> 32);
