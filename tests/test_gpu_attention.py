@@ -102,6 +102,12 @@ FUZZ = [
     ("bf16", 8, 8, 5, 1000, 8, 8, 64),
     ("bf16", 16, 2, 1, 513, 16, 1, 128),
     ("bf16", 24, 24, 1, 64, 2, 1, 64),
+    # plans with 3-8 key splits (split 0 also walks the in-pack tail), ragged and whole prefixes
+    ("bf16", 16, 12, 2, 1024, 32, 8, 128),
+    ("bf16", 16, 12, 2, 2500, 32, 8, 128),
+    ("bf16", 16, 4, 2, 700, 8, 2, 128),
+    ("bf16", 8, 3, 1, 1900, 8, 1, 128),
+    ("bf16", 24, 5, 3, 1300, 16, 4, 128),
     ("f32", 16, 4, 2, 100, 8, 2, 64),
     ("f32", 8, 3, 2, 0, 4, 4, 128),
 ]
