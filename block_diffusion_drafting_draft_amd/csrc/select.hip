@@ -377,6 +377,9 @@ struct SampTop2 {
   }
 };
 
+// Visits the thread's tokens of one chunk: f(z, id, word) for every token, or, where a whole
+// 16-byte vector's largest logit cannot reach floor_of() even with the largest Gumbel value, none of
+// the vector (its noise is not generated). floor_of() is re-read per vector: it rises as tokens pass.
 template <typename T, bool VEC, typename F, typename FLOOR>
 __device__ __forceinline__ void samp_walk(const SampArgs &a, const T *base, int begin, int end, uint32_t ctr_row,
                                           F &&f, FLOOR &&floor_of) {
