@@ -38,6 +38,9 @@ def _compare(z, T, seed, round_, got, row_index=None):
                 skipped += 1
                 continue
         assert int(got[r]) == want, (r, int(got[r]), want)
+    # near ties are rare (the two best of many continuous scores); a comparison that skipped most
+    # rows would prove nothing
+    assert skipped <= max(1, z.shape[0] // 10), skipped
     return skipped
 
 
