@@ -54,17 +54,26 @@ def _compare(zt, zd, tok, T, seed, round_, got, name):
     return flagged
 
 
+def _check_flag_share(flagged, total, name):
+    """Flagged draws (within the 1e-6 report window of a decision boundary; over a large vocabulary many
+    CDF steps are narrower than the window, so some are expected) are skipped in the token comparison;
+    a test that skipped most of its requests would prove nothing about the tokens."""
+    assert flagged <= max(1, total // 2), (name, flagged, total)
+
+
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_parity(name):
     require_gpu()
     w = synth.WORKLOADS[name]
     _say(f"verify parity: {name}")
     inp = synth.verify_inputs(w)
+    flagged = 0
     for round_ in range(3):
         got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], w.dtype, inp["temperature"],
                    inp["philox_seed"], round_)
-        _compare(inp["z_target"], inp["z_draft"], inp["tokens"], inp["temperature"], inp["philox_seed"],
-                 round_, got, f"{name} round {round_}")
+        flagged += _compare(inp["z_target"], inp["z_draft"], inp["tokens"], inp["temperature"],
+                            inp["philox_seed"], round_, got, f"{name} round {round_}")
+    _check_flag_share(flagged, 3 * inp["tokens"].shape[0], name)
 
 
 FUZZ = [
@@ -98,7 +107,8 @@ def test_fuzz(case):
             cut = (3 * i + 1) % B
             inp["tokens"][i, :cut] = np.argmax(inp["z_target"][i, :cut], axis=-1)
     got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], dtype, T, w.philox_seed, 5)
-    _compare(inp["z_target"], inp["z_draft"], inp["tokens"], T, w.philox_seed, 5, got, str(case))
+    flagged = _compare(inp["z_target"], inp["z_draft"], inp["tokens"], T, w.philox_seed, 5, got, str(case))
+    _check_flag_share(flagged, n_req, str(case))
     del base
 
 
@@ -142,7 +152,9 @@ def test_first_emitted_token_follows_target():
         first = np.where(got["n_accepted"] >= 1, tok[:, 0], got["next_token"])
         counts += np.bincount(first, minlength=V)
         if round_ == 0:
-            _compare(zt[:64], zd[:64], tok[:64], 1.0, 0xABC, 0, {k: v[:64] for k, v in got.items()}, "law subset")
+            f = _compare(zt[:64], zd[:64], tok[:64], 1.0, 0xABC, 0, {k: v[:64] for k, v in got.items()},
+                         "law subset")
+            _check_flag_share(f, 64, "law subset")
     p = special.softmax(zp[0].astype(np.float64))
     assert stats.chisquare(counts, p * counts.sum()).pvalue > 1e-3
 
@@ -174,7 +186,8 @@ def test_greedy_without_draft_logits():
         cut = (5 * i + 2) % 16
         inp["tokens"][i, :cut] = np.argmax(inp["z_target"][i, :cut], axis=-1)
     got = _run(inp["z_target"], None, inp["tokens"], "bf16", 0.0, w.philox_seed, 1)
-    _compare(inp["z_target"], None, inp["tokens"], 0.0, w.philox_seed, 1, got, "greedy, no draft logits")
+    f = _compare(inp["z_target"], None, inp["tokens"], 0.0, w.philox_seed, 1, got, "greedy, no draft logits")
+    _check_flag_share(f, inp["tokens"].shape[0], "greedy, no draft logits")
     del base
 
 
@@ -189,7 +202,9 @@ def test_masked_vocabulary_tail():
     zt[:, :, 27000:] = -np.inf
     zd[:, :, 27000:] = -np.inf
     tok = np.minimum(inp["tokens"], 26999).astype(np.int32)
+    flagged = 0
     for round_ in range(4):
         got = _run(zt, zd, tok, "bf16", 1.0, w.philox_seed, round_)
         assert np.all(got["next_token"] < 27000)
-        _compare(zt, zd, tok, 1.0, w.philox_seed, round_, got, f"masked tail round {round_}")
+        flagged += _compare(zt, zd, tok, 1.0, w.philox_seed, round_, got, f"masked tail round {round_}")
+    _check_flag_share(flagged, 4 * tok.shape[0], "masked tail")
