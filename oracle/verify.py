@@ -26,7 +26,9 @@ Readings (each listed in the design doc):
 * S(k) = prod_{j<k} alpha_j over 0-based rows, so S(k) is the paper's a_1...a_k; tau uses the
   alpha of every row whatever the sampled outcome.
 * T = 0 is greedy: alpha_j = 1 exactly when y_j is the first argmax of z^P_j, else 0; the
-  replacement (or bonus) is the first argmax of the target row. Draft logits are not read.
+  replacement (or bonus) is the first argmax of the target row. Draft logits are not read. A
+  target row whose logits are all -inf has no argmax: its draft is rejected and the emitted token
+  is -1 (no token), the value the drafting selection gives such a row.
 * Uniforms: u_j = Philox(seed; j, request, round, purpose 0); u' = Philox(seed; 0, request, round,
   purpose 1). Flags: bit 0 = some decision j <= j* had |u_j - alpha_j| < 1e-6; bit 1 =
   |u'Z - C(v*)| < 1e-6 Z or |u'Z - C(v*-1)| < 1e-6 Z; bit 2 = Z fallback.
@@ -66,13 +68,21 @@ def acceptance_ratios(z_target, z_draft, tokens, temperature):
     n_draft = tokens.size
     rows = np.arange(n_draft)
     if as_temperature(temperature) == 0.0:
-        return (np.argmax(z_target[:n_draft], axis=-1) == tokens).astype(np.float64)
+        return np.array([float(greedy_argmax(z_target[j]) == tokens[j]) for j in range(n_draft)])
     p = row_softmax(z_target[:n_draft], temperature)[rows, tokens]
     q = row_softmax(z_draft, temperature)[rows, tokens]
     alpha = np.ones(n_draft, dtype=np.float64)
     nz = q > 0
     alpha[nz] = np.minimum(1.0, p[nz] / q[nz])
     return alpha
+
+
+def greedy_argmax(row):
+    """First index of the largest logit, or -1 when every logit is -inf (no most likely token)."""
+    row = np.asarray(row)
+    if not np.any(row > -np.inf):
+        return -1
+    return int(np.argmax(row))
 
 
 def first_rejection(alpha, u):
@@ -148,9 +158,10 @@ def verify_request(z_target, z_draft, tokens, temperature, seed=0, round_=0, req
 
     if T == 0.0:
         row = z_target[j_star]
-        token = int(np.argmax(row))
+        token = greedy_argmax(row)
         mass = np.zeros(row.shape[-1])
-        mass[token] = 1.0
+        if token >= 0:
+            mass[token] = 1.0
         return Outcome(j_star, token, alpha, s, tau, 0, u_accept, u_sample, mass)
 
     decided = min(j_star, n_draft - 1)

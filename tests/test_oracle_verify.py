@@ -162,6 +162,22 @@ def test_greedy_ties_take_lowest_id():
     assert out.n_accepted == 1 and out.next_token == 2
 
 
+def test_greedy_masked_row_has_no_token():
+    """A target row of -inf logits has no most likely token: its draft is rejected and the emitted
+    token is -1; a row with any finite logit keeps the first argmax among them."""
+    zp = np.full((3, 5), -np.inf)
+    zp[0, 2] = 1.0
+    zp[2, [1, 4]] = -3.0
+    out = verify.verify_request(zp, np.zeros((2, 5)), [2, 0], 0.0)
+    assert out.n_accepted == 1 and out.next_token == -1
+    assert list(out.alpha) == [1.0, 0.0]
+    out = verify.verify_request(zp, np.zeros((2, 5)), [0, 0], 0.0)
+    assert out.n_accepted == 0 and out.next_token == 2
+    zp[1, 3] = -1e30
+    out = verify.verify_request(zp, np.zeros((2, 5)), [2, 3], 0.0)
+    assert out.n_accepted == 2 and out.next_token == 1
+
+
 def test_flags_mark_near_threshold_draws():
     rng = np.random.default_rng(13)
     zp, zq = _logits(rng, 4, 20)
