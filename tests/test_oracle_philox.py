@@ -40,6 +40,10 @@ def test_vectorised_matches_scalar():
 
 def test_uniform53_grid_and_range():
     assert philox.uniform53(0, 0) == 0.0
+    # word 0 supplies the 27 high bits, word 1 the 26 low bits (hand values)
+    assert philox.uniform53(0x80000000, 0) == 0.5
+    assert philox.uniform53(0, 0x80000000) == 2.0 ** -28
+    assert philox.uniform53(0x20, 0x40) == (2.0 ** 26 + 1.0) * 2.0 ** -53
     top = philox.uniform53(0xFFFFFFFF, 0xFFFFFFFF)
     assert top == 1.0 - 2.0**-53
     u = philox.uniforms(0xD3D2, np.arange(4096), 3, 9, 0)
@@ -54,3 +58,14 @@ def test_uniforms_chi_square():
     # distinct purposes / requests / rounds give independent-looking streams
     v = philox.uniforms(0xD3D0, np.arange(200000), 1, 0, 1)
     assert abs(np.corrcoef(u, v)[0, 1]) < 0.01
+
+
+def test_uniforms_layout_against_known_answers(golden):
+    """uniforms(seed, j, request, round, purpose) is the Philox block at counter (j, request, round,
+    purpose) under key (seed low word, seed high word), mapped by uniform53: checked on the
+    known-answer vectors, so the counter order and the key split are pinned too."""
+    for row in golden("philox4x32_10_kat.txt"):
+        words = [int(x, 16) for x in row]
+        ctr, key, want = words[:4], words[4:6], words[6:]
+        u = philox.uniforms(key[0] | (key[1] << 32), *ctr)
+        assert u == ((want[0] >> 5) * 2.0 ** 26 + (want[1] >> 6)) * 2.0 ** -53
