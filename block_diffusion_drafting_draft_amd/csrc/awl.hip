@@ -116,7 +116,9 @@ struct RefSum {
   template <int N>
   __device__ __forceinline__ void fold(const float (&z)[N]) {
     float part = group_sum(z);
-    if (!(part < 0x1p120f)) {
+    // the reference moves once a group's sum reaches 2^8: a kept term has an exponent argument
+    // below 8, whose relative fp32 rounding (|x| 2^-24) stays far below the weights' 1e-6 budget
+    if (!(part < 0x1p8f)) {
       float vm = z[0];
 #pragma unroll
       for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);

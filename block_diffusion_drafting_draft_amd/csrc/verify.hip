@@ -144,9 +144,12 @@ __device__ __forceinline__ int block_min_int(int v, int *sh) {
 // Per-thread accumulator of one row slice. Greedy: the running maximum and its first index.
 // Sampling: a reference value m (an element of the slice) and s = sum of exp((z - m)/T) relative to
 // it. The reference is not kept at the running maximum element by element: a later logit above it
-// simply contributes a term above 1. It moves up to a group's maximum only when the fp32 sum of a
-// group's terms would leave the range (an exponent near 128), so every term stays below e^84 and
-// the reference itself contributes exactly 1. Consumers only need some reference, not the maximum.
+// simply contributes a term above 1. It moves up to a group's maximum once a group's fp32 sum
+// reaches 2^8, so every term that is kept satisfies (z - m) log2(e)/T < 8. That bound is what keeps
+// the sum accurate: the fp32 rounding of the exponent argument x is relative, an error of about
+// |x| 2^-24 ln 2 in the term, and the terms that carry the row's mass are the ones near the top.
+// (Letting x grow to ~120 before moving, at T = 0.25 on a 151936-token row, put 3e-6 into alpha.)
+// Consumers only need some reference, not the maximum.
 template <bool GREEDY>
 struct RowAcc {
   float m = -INFINITY;
@@ -189,7 +192,7 @@ struct RowAcc {
         m = vm;
       }
       float part = group_sum(z, m, c_log2);
-      if (!(part < 0x1p120f)) {  // a logit far above the reference: move it to this group's max
+      if (!(part < 0x1p8f)) {  // a logit well above the reference: move it to this group's max
         const float vm = group_max(z);
         s *= exp_fp64((static_cast<double>(m) - vm) * inv_t);
         m = vm;
@@ -381,6 +384,7 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
   double alpha = 1.0, u = 1.0;
   if (j < nd) {
     if (a.greedy) {
+      // a row of -inf logits has no argmax (INT_MAX): its draft is rejected
       alpha = (rr.tok[j] == rr.arg[j]) ? 1.0 : 0.0;
     } else {
       // P_j(y) = exp((z_y - ref)/T) / sum_j, likewise Q_j(y)
@@ -422,14 +426,14 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
       if (a.tau) a.tau[i] = static_cast<float>(1.0 + tsum);
       if (a.flags) a.flags[i] = near ? 1u : 0u;
       if (a.greedy) {
-        a.next_token[i] = rr.arg[n_acc];
+        a.next_token[i] = rr.arg[n_acc] == INT_MAX ? -1 : rr.arg[n_acc];  // -1: every logit is -inf
       } else {
         a.state[i] = st;
       }
     }
   }
   // greedy: the outcome is final here (sampling matches after its draw)
-  if (store && a.greedy && a.hit) match_outcome(a, i, n_acc, rr.arg[n_acc]);
+  if (store && a.greedy && a.hit) match_outcome(a, i, n_acc, rr.arg[n_acc] == INT_MAX ? -1 : rr.arg[n_acc]);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -1,8 +1,9 @@
 """GPU parity of spec_verify against the oracle under shared Philox uniforms (through the C ABI).
 
-Bar: n_accepted and next_token bit-exact, except on draws the oracle flags as within 1e-6 of a
-threshold (counted and printed); |alpha - alpha_oracle| < 1e-6; tau within a relative 1e-5;
-survival within 1e-5 absolute."""
+Bar: n_accepted and next_token bit-exact on every draw whose outcome the arithmetic decides (see
+_compare), flags bits 0-2 checked against the oracle's distances; |alpha - alpha_oracle| < 1e-6; tau
+within a relative 1e-5; survival within 1e-5 absolute. Full-vocabulary workloads compare 16
+requests x 4 rounds each (256 draws at V = 151936)."""
 
 import sys
 
@@ -32,48 +33,102 @@ def _run(zt, zd, tok, dtype, T, seed, round_):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def _compare(zt, zd, tok, T, seed, round_, got, name):
+# Flag bands: the library reports a draw within 1e-6 of a threshold (bit 0: |u_j - alpha_j| on a
+# decided row; bit 1: |u'Z - C| / Z at the sampled token's CDF step). Its alpha differs from the
+# oracle's by well under 0.5e-6 and its CDF by far less, so an oracle distance below 0.5e-6 must be
+# reported and one above 2e-6 must not be.
+BAND_SET, BAND_CLEAR = 0.5e-6, 2e-6
+# Window of a sampled draw that fp64 on both sides may legitimately decide differently: relative to Z,
+# plus an absolute floor for the cancellation in max(0, P - Q) (both sides normalise P and Q to 1).
+SAMPLE_WINDOW_REL, SAMPLE_WINDOW_ABS = 1e-9, 1e-12
+
+
+def _compare(zt, zd, tok, T, seed, round_, got, name, counts=None):
+    """Element-wise comparison of one call with the oracle.
+
+    Every draw is compared unless the arithmetic itself leaves its outcome open: an acceptance test
+    whose oracle distance |u_j - alpha_j| is within the measured alpha error of this very row (the
+    library's fp32-stored alpha against the oracle's, plus the fp32 rounding of the stored value), or
+    a sample whose u'Z lies within SAMPLE_WINDOW of a CDF step. Such draws are counted as "open"; the
+    flags of every compared draw are checked against the bands above."""
     n_req = tok.shape[0]
-    flagged = mism = 0
+    flagged = open_ = compared = 0
+    greedy = float(np.float32(T)) == 0.0
     for i in range(n_req):
         o = o_ver.verify_request(zt[i], None if zd is None else zd[i], tok[i], T, seed, round_, i)
-        np.testing.assert_array_less(np.abs(got["alpha"][i] - o.alpha), 1e-6)
+        a_gpu = got["alpha"][i].astype(np.float64)
+        err = np.abs(a_gpu - o.alpha)
+        np.testing.assert_array_less(err, 1e-6)
         np.testing.assert_array_less(np.abs(got["survival"][i] - o.survival), 1e-5)
         assert abs(got["tau"][i] - o.tau) <= 1e-5 * o.tau, (i, got["tau"][i], o.tau)
-        near_acc = bool(o.flags & o_ver.FLAG_NEAR_ACCEPT)
-        near_smp = bool(o.flags & o_ver.FLAG_NEAR_SAMPLE)
-        if near_acc or near_smp:
+        n_acc, token, fl = int(got["n_accepted"][i]), int(got["next_token"][i]), int(got["flags"][i])
+        if o.flags & (o_ver.FLAG_NEAR_ACCEPT | o_ver.FLAG_NEAR_SAMPLE):
             flagged += 1
-            if got["n_accepted"][i] != o.n_accepted or got["next_token"][i] != o.next_token:
-                mism += 1
+        nd = tok.shape[1]
+        decided = min(o.n_accepted, nd - 1)
+        dist_a = np.abs(o.u_accept[:decided + 1] - o.alpha[:decided + 1])
+        if greedy:
+            assert fl == 0, (name, i, fl)
+            assert (n_acc, token) == (o.n_accepted, o.next_token), (name, i, n_acc, token, o.n_accepted,
+                                                                   o.next_token)
+            compared += 1
             continue
-        assert got["n_accepted"][i] == o.n_accepted, (name, i, got["n_accepted"][i], o.n_accepted)
-        assert got["next_token"][i] == o.next_token, (name, i, got["next_token"][i], o.next_token)
-        assert (got["flags"][i] & 4) == (o.flags & 4)
-    _say(f"  {name}: {n_req} requests, {flagged} oracle-flagged draws, {mism} of them differ")
-    return flagged
+        if np.any(dist_a <= err[:decided + 1] + 2.0 ** -24):
+            open_ += 1  # the library's own alpha may fall on the other side of u_j
+            continue
+        assert n_acc == o.n_accepted, (name, i, n_acc, o.n_accepted)
+        # bit 0 against the oracle's distance over the decided rows
+        if dist_a.min() < BAND_SET:
+            assert fl & 1, (name, i, "near-accept not reported", dist_a.min())
+        if dist_a.min() > BAND_CLEAR:
+            assert not fl & 1, (name, i, "near-accept reported", dist_a.min())
+        assert (fl & 4) == (o.flags & 4), (name, i, fl, o.flags)
+        c = np.cumsum(o.sample_mass)
+        z = float(c[-1])
+        target = o.u_sample * z
+        v = o.next_token
+        c_prev = float(c[v - 1]) if v > 0 else 0.0
+        dist_s = min(abs(target - float(c[v])), abs(target - c_prev))
+        if dist_s <= SAMPLE_WINDOW_REL * z + SAMPLE_WINDOW_ABS:
+            open_ += 1
+            continue
+        assert token == v, (name, i, token, v, dist_s / z)
+        if dist_s < BAND_SET * z:
+            assert fl & 2, (name, i, "near-sample not reported", dist_s / z)
+        if dist_s > BAND_CLEAR * z:
+            assert not fl & 2, (name, i, "near-sample reported", dist_s / z)
+        compared += 1
+    _say(f"  {name}: {n_req} draws, {compared} compared bit-exactly, {flagged} oracle-flagged "
+         f"(all compared unless open), {open_} left open by the arithmetic")
+    if counts is not None:
+        counts["compared"] += compared
+        counts["open"] += open_
+        counts["flagged"] += flagged
+        counts["total"] += n_req
+    return open_
 
 
-def _check_flag_share(flagged, total, name):
-    """Flagged draws (within the 1e-6 report window of a decision boundary; over a large vocabulary many
-    CDF steps are narrower than the window, so some are expected) are skipped in the token comparison;
-    a test that skipped most of its requests would prove nothing about the tokens."""
-    assert flagged <= max(1, total // 2), (name, flagged, total)
+def _check_open(open_, total, name):
+    """A draw is left open only when the arithmetic's own error reaches it (probability ~1e-7 per
+    acceptance test, ~1e-9 per sample): with fixed seeds, none is expected."""
+    assert open_ == 0, (name, open_, total)
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_parity(name):
     require_gpu()
     w = synth.WORKLOADS[name]
-    _say(f"verify parity: {name}")
-    inp = synth.verify_inputs(w)
-    flagged = 0
-    for round_ in range(3):
+    _say(f"verify parity: {name}, 16 requests x 4 rounds")
+    inp = synth.verify_inputs(w, n_req=16)
+    counts = dict(compared=0, open=0, flagged=0, total=0)
+    for round_ in range(4):
         got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], w.dtype, inp["temperature"],
                    inp["philox_seed"], round_)
-        flagged += _compare(inp["z_target"], inp["z_draft"], inp["tokens"], inp["temperature"],
-                            inp["philox_seed"], round_, got, f"{name} round {round_}")
-    _check_flag_share(flagged, 3 * inp["tokens"].shape[0], name)
+        _compare(inp["z_target"], inp["z_draft"], inp["tokens"], inp["temperature"],
+                 inp["philox_seed"], round_, got, f"{name} round {round_}", counts)
+    _say(f"  {name}: {counts}")
+    assert counts["compared"] == 64, counts
+    _check_open(counts["open"], counts["total"], name)
 
 
 FUZZ = [
@@ -89,6 +144,11 @@ FUZZ = [
     ("f32", 2, 8, 3000, 0.02, "iid"),
     ("bf16", 2, 16, 151936, 0.0, "zipf"),  # greedy
     ("f32", 6, 8, 50, 0.0, "iid"),        # greedy, small
+    # low temperatures over the full vocabulary: the scaled logits of the Zipf rows span hundreds of
+    # log2 units, where the statistics pass's reference logit has to follow the row's top
+    ("bf16", 4, 16, 151936, 0.25, "zipf"),
+    ("bf16", 4, 16, 151936, 0.3, "zipf"),
+    ("bf16", 4, 16, 151936, 0.5, "zipf"),
 ]
 
 
@@ -107,8 +167,8 @@ def test_fuzz(case):
             cut = (3 * i + 1) % B
             inp["tokens"][i, :cut] = np.argmax(inp["z_target"][i, :cut], axis=-1)
     got = _run(inp["z_target"], inp["z_draft"], inp["tokens"], dtype, T, w.philox_seed, 5)
-    flagged = _compare(inp["z_target"], inp["z_draft"], inp["tokens"], T, w.philox_seed, 5, got, str(case))
-    _check_flag_share(flagged, n_req, str(case))
+    open_ = _compare(inp["z_target"], inp["z_draft"], inp["tokens"], T, w.philox_seed, 5, got, str(case))
+    _check_open(open_, n_req, str(case))
     del base
 
 
@@ -154,7 +214,7 @@ def test_first_emitted_token_follows_target():
         if round_ == 0:
             f = _compare(zt[:64], zd[:64], tok[:64], 1.0, 0xABC, 0, {k: v[:64] for k, v in got.items()},
                          "law subset")
-            _check_flag_share(f, 64, "law subset")
+            _check_open(f, 64, "law subset")
     p = special.softmax(zp[0].astype(np.float64))
     assert stats.chisquare(counts, p * counts.sum()).pvalue > 1e-3
 
@@ -187,7 +247,7 @@ def test_greedy_without_draft_logits():
         inp["tokens"][i, :cut] = np.argmax(inp["z_target"][i, :cut], axis=-1)
     got = _run(inp["z_target"], None, inp["tokens"], "bf16", 0.0, w.philox_seed, 1)
     f = _compare(inp["z_target"], None, inp["tokens"], 0.0, w.philox_seed, 1, got, "greedy, no draft logits")
-    _check_flag_share(f, inp["tokens"].shape[0], "greedy, no draft logits")
+    _check_open(f, inp["tokens"].shape[0], "greedy, no draft logits")
     del base
 
 
@@ -202,9 +262,60 @@ def test_masked_vocabulary_tail():
     zt[:, :, 27000:] = -np.inf
     zd[:, :, 27000:] = -np.inf
     tok = np.minimum(inp["tokens"], 26999).astype(np.int32)
-    flagged = 0
+    open_ = 0
     for round_ in range(4):
         got = _run(zt, zd, tok, "bf16", 1.0, w.philox_seed, round_)
         assert np.all(got["next_token"] < 27000)
-        flagged += _compare(zt, zd, tok, 1.0, w.philox_seed, round_, got, f"masked tail round {round_}")
-    _check_flag_share(flagged, 4 * tok.shape[0], "masked tail")
+        open_ += _compare(zt, zd, tok, 1.0, w.philox_seed, round_, got, f"masked tail round {round_}")
+    _check_open(open_, 4 * tok.shape[0], "masked tail")
+
+
+def test_every_emitted_position_follows_target():
+    """Losslessness over the whole emitted sequence on the GPU, 2^20 draws at T = 0.7: with drafts
+    drawn from Q_j and logit rows that do not depend on the history, the token emitted at position
+    k (the accepted draft y_k for k < n_acc, the residual draw at k = n_acc, the bonus at k = B-1)
+    follows P_k whenever position k is emitted. One chi-square test per position."""
+    require_gpu()
+    _say("verify: every emitted position ~ P_k over 2^20 draws, T = 0.7")
+    rng = np.random.default_rng(16)
+    B, V, n_req, rounds, T = 4, 12, 16384, 64, 0.7
+    zp = synth.round_bf16(rng.normal(0, 1.0, size=(B, V)).astype(np.float32))
+    zq = synth.round_bf16((zp[:B - 1] + rng.normal(0, 0.8, size=(B - 1, V))).astype(np.float32))
+    zt = np.broadcast_to(zp, (n_req, B, V)).copy()
+    zd = np.broadcast_to(zq, (n_req, B - 1, V)).copy()
+    p = special.softmax(zp.astype(np.float64) / np.float64(np.float32(T)), axis=-1)
+    q = special.softmax(zq.astype(np.float64) / np.float64(np.float32(T)), axis=-1)
+    counts = np.zeros((B, V))
+    t = dev(zt, "bf16")
+    d = dev(zd, "bf16")
+    for round_ in range(rounds):
+        tok = np.stack([rng.choice(V, size=n_req, p=q[j]) for j in range(B - 1)], axis=1).astype(np.int32)
+        out = _binding.spec_verify(t, d, torch.from_numpy(tok).cuda(), T, 0x5EC, round_)
+        n_acc = out["n_accepted"].cpu().numpy()
+        nxt = out["next_token"].cpu().numpy()
+        for k in range(B):
+            emitted = n_acc >= k
+            val = np.where(n_acc > k, tok[:, min(k, B - 2)], nxt)[emitted]
+            counts[k] += np.bincount(val, minlength=V)
+    for k in range(B):
+        n = counts[k].sum()
+        pv = stats.chisquare(counts[k], p[k] * n).pvalue
+        _say(f"  position {k}: {int(n)} emitted, chi-square p = {pv:.3g}")
+        assert pv > 1e-3, (k, pv)
+
+
+def test_greedy_masked_row():
+    """Greedy verify over a target row of -inf logits: that row's draft is rejected and the emitted
+    token is -1, as the oracle gives; rows before it keep their argmax decisions."""
+    require_gpu()
+    _say("verify: greedy over a fully masked target row")
+    rng = np.random.default_rng(17)
+    n_req, B, V = 3, 8, 4096
+    zt = synth.round_bf16(rng.normal(0, 1, size=(n_req, B, V)).astype(np.float32))
+    tok = np.argmax(zt[:, :B - 1], axis=-1).astype(np.int32)
+    for i, row in enumerate([2, 5, 7]):  # the last request masks its bonus row
+        zt[i, row] = -np.inf
+    got = _run(zt, None, tok, "bf16", 0.0, 3, 0)
+    _compare(zt, None, tok, 0.0, 3, 0, got, "greedy, masked rows")
+    assert list(got["next_token"]) == [-1, -1, -1], got["next_token"]
+    assert list(got["n_accepted"]) == [2, 5, 7], got["n_accepted"]
