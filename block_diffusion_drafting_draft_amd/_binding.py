@@ -243,6 +243,16 @@ def draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, r
     return out
 
 
+def draft_attn_packed_join(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, req_prefix_len, block_size,
+                           join, **kw):
+    """draft_attn_packed whose stream waits for the recorded torch.cuda.Event `join` before the call's
+    last launch (the C entry point of the same name)."""
+    if join is None:
+        raise ValueError("draft_attn_packed_join needs a recorded event")
+    return draft_attn_packed(q, k_new, v_new, k_cache, v_cache, descs, req_block_off, req_prefix_len, block_size,
+                             join=join, **kw)
+
+
 def spec_verify_workspace(n_req, n_draft, vocab):
     return int(load().spec_verify_workspace(n_req, n_draft, vocab))
 
@@ -298,6 +308,14 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, ro
                                   _stream(stream))
     _check(st, "spec_verify_match")
     return out
+
+
+def spec_verify_match(target_logits, draft_logits, draft_tokens, temperature, seed, round_, descs, req_block_off,
+                      **kw):
+    """spec_verify with the cache match inside its launches (the C entry point of the same name):
+    the returned dict also holds hit_branch."""
+    return spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, round_,
+                       match=(descs, req_block_off), **kw)
 
 
 def branch_cache_match(descs, req_block_off, n_accepted, next_token, hit=None, stream=None):

@@ -7,8 +7,9 @@
 // or rows up to itself for a causal block), with grouped-query heads.
 //
 // Design:
-//  * A workgroup (4 wavefronts) owns 128 query-head rows that share one key/value head: with group
-//    size G = H_q / H_kv, 128/G queries x G heads. Each wavefront owns 32 rows.
+//  * A bf16 workgroup (8 wavefronts, one workgroup per compute unit) owns 256 query-head rows that
+//    share one key/value head: with group size G = H_q / H_kv, 256/G queries x G heads. Each
+//    wavefront owns 32 rows; two wavefronts share a SIMD. (fp32: 4 wavefronts, 128 rows.)
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16: Q stays in registers (the B operand)
 //    for the whole key walk, K and V come from LDS. The S^T accumulator leaves every lane holding one
 //    query column, so the softmax row max / sum are per-lane scalars (one cross-half exchange), and
@@ -19,8 +20,9 @@
 //    patterns below conflict-free. K fragments are plain 16-byte reads; V^T fragments come from the
 //    transposing LDS read ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one column
 //    -- exactly the key order the S^T accumulator holds, so no data is permuted anywhere.
-//  * Prefix phase: double-buffered tiles over the request's prefix (one barrier per tile), no mask
-//    except the ragged end; every packed query of the request shares this one walk.
+//  * Prefix phase: a four-stage ring of LDS tiles over the request's prefix (three copies in flight
+//    ahead of the tile being computed, one barrier per tile), no mask except the ragged end; every
+//    packed query of the request shares this one walk.
 //  * In-pack tail: the rows of the request's current block and of the blocks the tile's queries
 //    belong to are gathered into 64-key tiles with a per-(row, key) visibility test from the block
 //    descriptors.

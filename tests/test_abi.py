@@ -37,6 +37,18 @@ def test_library_exports_every_declared_symbol():
     assert set(_binding.EXPORTS) == set(_declared_functions())
 
 
+def test_binding_has_every_entry_point_by_name():
+    """The Python binding carries a function of the same name for every declared entry point, and the
+    package re-exports each of them."""
+    import block_diffusion_drafting_draft_amd as pkg
+    for name in _declared_functions():
+        if name == "d3d_status_string":
+            continue
+        assert callable(getattr(_binding, name, None)), name
+        assert name in pkg.__all__, name
+        assert getattr(pkg, name) is getattr(_binding, name)
+
+
 @pytest.mark.parametrize("B,C,F,L", [(16, 12, 2, 4096), (32, 16, 5, 8192), (4, 3, 1, 0), (8, 8, 3, 7)])
 def test_descriptor_builder_matches_oracle_packing(B, C, F, L):
     rng = np.random.default_rng(B * 100 + C)
@@ -139,3 +151,4 @@ def test_topk_workspace():
     assert _binding.draft_topk_workspace(1, 7, 8) == 256
     for bad in ((0, 10, 1), (1, 0, 1), (1, 10, 0), (1, 10, 9)):
         assert _binding.draft_topk_workspace(*bad) == 0
+
