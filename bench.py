@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    p.add_argument("--no-serve-verify", action="store_true",
+                   help="skip the serving batch's verify measurement (warm and cold)")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the next-row measurements (token selection, KV commit, AWL, training attention)")
     p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss",
@@ -366,26 +368,9 @@ def main():
     names = ("draft_attn_packed", "spec_verify", "branch_cache_match", "round")
     t_attn, t_ver, t_match, t_round = (mean_us(graphs[n], reps) for n in names)
     stats = {n: summary(per_replay_us(graphs[n], reps)) for n in names}
-    # cold verify: before every timed call the MALL is flushed by reading 512 MiB (untimed; a read
-    # leaves no dirty lines whose write-back would compete with the timed reads), and the logits
-    # rotate over three copies
-    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    sink = torch.empty((), dtype=torch.float32, device="cuda")
-    copies = [(r.z_t.clone(), r.z_d.clone(), r.tokens.clone()) for _ in range(3)]
-    cold_graphs = []
-    for zt, zd, tok in copies:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            r.lib.spec_verify(zt, zd, tok, r.vin["temperature"], r.vin["philox_seed"], r.round, ws=r.ver_ws,
-                              out=r.ver_out)
-        cold_graphs.append(g)
-    torch.cuda.synchronize()
-    cold = []
-    for k in range(reps):
-        torch.sum(flush, dim=0, out=sink)
-        cold.append(per_replay_us(cold_graphs[k % 3], 1, warmup=0)[0])
-    t_ver_cold = summary(np.array(cold))
-    del flush, sink, copies, cold_graphs
+    t_ver_cold = summary(verify_cold_us(r.lib, r.z_t, r.z_d, r.tokens, r.vin["temperature"], r.vin["philox_seed"],
+                                        r.round, r.ver_ws, r.ver_out, per_replay_us, reps))
+    serve = None if args.no_serve_verify else verify_serve(torch, mean_us, per_replay_us, summary, reps)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(cur)
@@ -446,6 +431,8 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},
     }
+    if serve is not None:
+        out["verify_serve"] = serve
     if not args.no_next_rows:
         out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
                             "kv_commit": next_row_commit(r, torch, mean_us),
@@ -455,6 +442,61 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def verify_cold_us(lib, zt, zd, tokens, temperature, seed, round_, ws, out, per_replay_us, reps):
+    """HIP-event duration (µs) of `reps` spec_verify calls, each after the MALL has been flushed by
+    reading 512 MiB (untimed; a read leaves no dirty lines whose write-back would compete with the
+    timed reads), the logits rotating over three copies."""
+    import torch
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    copies = [(zt.clone(), zd.clone(), tokens.clone()) for _ in range(3)]
+    graphs = []
+    for a, b, c in copies:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            lib.spec_verify(a, b, c, temperature, seed, round_, ws=ws, out=out)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    cold = []
+    for k in range(reps):
+        torch.sum(flush, dim=0, out=sink)
+        cold.append(per_replay_us(graphs[k % 3], 1, warmup=0)[0])
+    del flush, sink, copies, graphs
+    return np.array(cold)
+
+
+def verify_serve(torch, mean_us, per_replay_us, summary, reps):
+    """spec_verify on the serving batch's verify (16 requests x (16 target + 15 draft rows) over
+    V = 151936, bf16: 150,720,512 bytes), the configuration the HBM bar is judged on: warm (mean of
+    back-to-back replays) and cold (MALL flushed before each call, median)."""
+    from block_diffusion_drafting_draft_amd import _binding, synth
+    w = synth.WORKLOADS["serve-16req-B16C12F2-paged16-V151936"]
+    vin = synth.verify_inputs(w)
+    cu = lambda x: torch.from_numpy(synth.f32_to_bf16_bits(x).view(np.int16).copy()).view(torch.bfloat16).cuda()
+    zt, zd = cu(vin["z_target"]), cu(vin["z_draft"])
+    tok = torch.from_numpy(vin["tokens"]).cuda()
+    n_req, nd = tok.shape
+    ws = torch.empty(_binding.spec_verify_workspace(n_req, nd, w.vocab), dtype=torch.uint8, device="cuda")
+    out = _binding.spec_verify(zt, zd, tok, vin["temperature"], vin["philox_seed"], 0, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _binding.spec_verify(zt, zd, tok, vin["temperature"], vin["philox_seed"], 0, ws=ws, out=out)
+    warm = mean_us(g, reps)
+    cold = summary(verify_cold_us(_binding, zt, zd, tok, vin["temperature"], vin["philox_seed"], 0, ws, out,
+                                  per_replay_us, reps))
+    nbytes = 2 * n_req * (2 * nd + 1) * w.vocab + 4 * n_req * nd + n_req * (4 + 4 + 4 * nd + 4 * nd + 4 + 4)
+    del g, zt, zd, tok, ws, out
+    gbs = lambda t: nbytes / (t * 1e-6) / 1e9
+    return {"workload": w.name, "bytes": nbytes,
+            "warm_us": round(warm, 3), "warm_gbs": round(gbs(warm), 1),
+            "warm_pct_hbm_peak": round(100 * gbs(warm) / HBM_PEAK_GBS, 2),
+            "cold_us": round(cold[0], 3), "cold_p10_p90": [round(cold[1], 3), round(cold[2], 3)],
+            "cold_gbs": round(gbs(cold[0]), 1), "cold_pct_hbm_peak": round(100 * gbs(cold[0]) / HBM_PEAK_GBS, 2),
+            "protocol": "warm: mean of 100 back-to-back graph replays; cold: 512 MiB read before each call "
+                        "(untimed), logits rotating over 3 copies, HIP events around each call, median of 100"}
 
 
 def awl_graph(r, torch, n_blocks=128, n_pos=15):
