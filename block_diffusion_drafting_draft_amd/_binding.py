@@ -48,6 +48,9 @@ _SIGNATURES = {
                                      _c.c_int, _c.c_float, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
                                      _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                      _c.c_size_t, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "spec_verify_noalloc": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                                       _c.c_int, _c.c_float, _c.c_uint64, _c.c_uint32, _c.c_void_p, _c.c_void_p,
+                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "branch_cache_match": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "draft_topk_workspace": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
@@ -307,6 +310,38 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, ro
     st = load().spec_verify_match(*args, _ptr(descs), descs.shape[0], _ptr(req_block_off), _ptr(out["hit_branch"]),
                                   _stream(stream))
     _check(st, "spec_verify_match")
+    return out
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, seed, round_, out=None,
+                        stream=None):
+    """spec_verify whose workspace is the library's static per-GPU scratch (the C entry point of the
+    same name allocates nothing; calls that overlap on one GPU race). Arguments and the returned
+    dict as spec_verify; `out` may hold preallocated output tensors."""
+    _dev(target_logits, "target_logits")
+    _dev(draft_tokens, "draft_tokens")
+    dt = _dtype_code(target_logits)
+    n_req, b, vocab = target_logits.shape
+    nd = b - 1
+    if draft_tokens.dtype != torch.int32 or draft_tokens.shape != (n_req, nd):
+        raise ValueError("draft_tokens must be int32 [n_req, B-1]")
+    if float(temperature) != 0.0 or draft_logits is not None:
+        _dev(draft_logits, "draft_logits")
+        if draft_logits.dtype != target_logits.dtype or draft_logits.shape != (n_req, nd, vocab):
+            raise ValueError("draft_logits must match target_logits' dtype and be [n_req, B-1, V]")
+    dev = target_logits.device
+    if out is None:
+        out = dict(n_accepted=torch.empty(n_req, dtype=torch.int32, device=dev),
+                   next_token=torch.empty(n_req, dtype=torch.int32, device=dev),
+                   alpha=torch.empty(n_req, nd, dtype=torch.float32, device=dev),
+                   survival=torch.empty(n_req, nd, dtype=torch.float32, device=dev),
+                   tau=torch.empty(n_req, dtype=torch.float32, device=dev),
+                   flags=torch.empty(n_req, dtype=torch.int32, device=dev))
+    st = load().spec_verify_noalloc(dt, _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), n_req, nd,
+                                    vocab, float(temperature), int(seed) & (2**64 - 1), int(round_) & 0xFFFFFFFF,
+                                    _ptr(out["n_accepted"]), _ptr(out["next_token"]), _ptr(out["alpha"]),
+                                    _ptr(out["survival"]), _ptr(out["tau"]), _ptr(out["flags"]), _stream(stream))
+    _check(st, "spec_verify_noalloc")
     return out
 
 

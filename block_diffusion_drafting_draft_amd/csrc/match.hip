@@ -88,6 +88,7 @@ extern "C" const char *d3d_status_string(int status) {
     case D3D_EUNSUPPORTED: return "unsupported configuration";
     case D3D_EHIP: return "HIP launch error";
     case D3D_EWORKSPACE: return "workspace missing or too small";
+    case D3D_ESCRATCH: return "the call needs more workspace than the allocation-free entry point's static scratch";
     default: return "unknown status";
   }
 }

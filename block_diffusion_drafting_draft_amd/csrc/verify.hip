@@ -29,6 +29,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "d3d_internal.h"
 
@@ -894,4 +896,60 @@ extern "C" int spec_verify_match(d3d_dtype dtype, const void *target_logits, con
   return d3d::verify_impl(dtype, target_logits, draft_logits, draft_tokens, n_req, n_draft, vocab, temperature, seed,
                           round, n_accepted, next_token, alpha, survival, tau, flags, ws, ws_bytes, descs,
                           total_blocks, req_block_off, hit_branch, stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+// allocation-free variant: the workspace lives in a file-scope device array
+// ------------------------------------------------------------------------------------------------
+// One copy per GPU (held until the process ends). Its host-side name is only a stand-in for the
+// device address: host code uses the address hipGetSymbolAddress returns on each device, never the
+// name. Nothing in the verify workspace needs initial contents, so no call clears it.
+static __device__ __align__(256) unsigned char scratch[D3D_VERIFY_SCRATCH_BYTES];
+
+namespace d3d {
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device, looked up once per device.
+int scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return D3D_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return D3D_EUNSUPPORTED;
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return D3D_EHIP;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return D3D_OK;
+}
+}  // namespace
+}  // namespace d3d
+
+extern "C" int spec_verify_noalloc(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                                   const int32_t *draft_tokens, int n_req, int n_draft, int vocab,
+                                   float temperature, uint64_t seed, uint32_t round, int32_t *n_accepted,
+                                   int32_t *next_token, float *alpha, float *survival, float *tau,
+                                   uint32_t *flags, hipStream_t stream) {
+  d3d::VerifyPlan p;
+  if (d3d::plan_verify(n_req, n_draft, vocab, &p) != D3D_OK) return D3D_EINVAL;
+  if (p.total > D3D_VERIFY_SCRATCH_BYTES) return D3D_ESCRATCH;  // checked before anything else runs
+  void *ws = nullptr;
+  const int st = d3d::scratch_ptr(&ws);
+  if (st != D3D_OK) return st;
+  return d3d::verify_impl(dtype, target_logits, draft_logits, draft_tokens, n_req, n_draft, vocab, temperature,
+                          seed, round, n_accepted, next_token, alpha, survival, tau, flags, ws,
+                          D3D_VERIFY_SCRATCH_BYTES, nullptr, 0, nullptr, nullptr, stream);
 }

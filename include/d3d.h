@@ -14,8 +14,9 @@
  *    (bf16 = IEEE bfloat16 bit patterns, f32 = IEEE binary32) unless stated otherwise.
  *  - Return value: D3D_OK (0) or a negative status. Argument errors are found on the host before
  *    anything is launched; d3d_status_string() describes a status. No C++ exception crosses the
- *    ABI. The library holds no global mutable state and is thread-safe; two calls that share a
- *    workspace must not overlap in time.
+ *    ABI. The library is thread-safe; two calls that share a workspace must not overlap in time.
+ *    Its only global state is the static scratch of spec_verify_noalloc (one array per GPU, and
+ *    the cached device address of that array).
  *  - Device-side contents (descriptors, page tables, token ids) are not validated on the host;
  *    kernels clamp every index they derive from them so that no access leaves its buffer.
  */
@@ -35,7 +36,8 @@ enum {
   D3D_EINVAL = -1,       /* bad shape or argument; nothing launched */
   D3D_EUNSUPPORTED = -2, /* valid but not implemented (head_dim, group size, ...) */
   D3D_EHIP = -3,         /* a HIP launch reported an error */
-  D3D_EWORKSPACE = -4    /* workspace missing or smaller than the *_workspace() size */
+  D3D_EWORKSPACE = -4,   /* workspace missing or smaller than the *_workspace() size */
+  D3D_ESCRATCH = -5      /* spec_verify_noalloc: the call needs more than D3D_VERIFY_SCRATCH_BYTES */
 };
 
 typedef enum { D3D_BF16 = 0, D3D_F32 = 1 } d3d_dtype;
@@ -185,6 +187,25 @@ int spec_verify(d3d_dtype dtype, const void *target_logits, const void *draft_lo
                 uint64_t seed, uint32_t round, int32_t *n_accepted, int32_t *next_token,
                 float *alpha, float *survival, float *tau, uint32_t *flags, void *ws,
                 size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * spec_verify for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments and outputs as spec_verify,
+ * without ws / ws_bytes. The workspace is a file-scope device array of D3D_VERIFY_SCRATCH_BYTES on
+ * each GPU, held until the process ends; the call allocates and frees nothing. Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (different streams, or different
+ * host threads without ordering) race and give undefined outputs. Its contents carry over from
+ * call to call; none of them is read before it is written, so nothing is cleared.
+ * Errors: as spec_verify; D3D_ESCRATCH (nothing launched) when spec_verify_workspace(n_req,
+ * n_draft, vocab) exceeds D3D_VERIFY_SCRATCH_BYTES (e.g. about 1700 requests of B = 16 at
+ * V = 151936); D3D_EHIP if the array's device address cannot be obtained.
+ * ------------------------------------------------------------------------------------------- */
+#define D3D_VERIFY_SCRATCH_BYTES ((size_t)4 << 20)
+
+int spec_verify_noalloc(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
+                        const int32_t *draft_tokens, int n_req, int n_draft, int vocab, float temperature,
+                        uint64_t seed, uint32_t round, int32_t *n_accepted, int32_t *next_token,
+                        float *alpha, float *survival, float *tau, uint32_t *flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Branch-cache match ([D3D] 前置知识: 异步起草与缓存命中): a verified outcome (n_acc accepted

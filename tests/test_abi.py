@@ -152,3 +152,16 @@ def test_topk_workspace():
     for bad in ((0, 10, 1), (1, 0, 1), (1, 10, 0), (1, 10, 9)):
         assert _binding.draft_topk_workspace(*bad) == 0
 
+
+def test_noalloc_verify_rejects_calls_beyond_its_scratch():
+    """spec_verify_noalloc checks the call's workspace against its static scratch on the host and
+    returns D3D_ESCRATCH before anything runs (the pointers below are never dereferenced)."""
+    lib = _binding.load()
+    n_req, nd, V = 4096, 15, 151936
+    need = lib.spec_verify_workspace(n_req, nd, V)
+    assert need > (4 << 20)
+    fake = ctypes.c_void_p(1 << 40)
+    st = lib.spec_verify_noalloc(_binding.D3D_BF16, fake, fake, fake, n_req, nd, V, 1.0, 1, 0, fake, fake, None,
+                                 None, None, None, None)
+    assert st == -5
+    assert b"scratch" in lib.d3d_status_string(st)
