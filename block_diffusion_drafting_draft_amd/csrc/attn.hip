@@ -763,11 +763,11 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   if (D != 64 && D != 128) return D3D_EUNSUPPORTED;
   if (off[0] != 0) return D3D_EINVAL;
   for (int i = 0; i < n_req; ++i) {
-    if (off[i + 1] < off[i] || pre[i] < 0) return D3D_EINVAL;
+    if (off[i + 1] < off[i] || pre[i] < 0 || pre[i] > kMaxPrefix) return D3D_EINVAL;
   }
   const long long total_q = static_cast<long long>(off[n_req]) * B;
   // packed rows are addressed with 32-bit byte offsets (buffer loads)
-  if (total_q * Hkv * D * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;
+  if (total_q >= (1ll << 31) || Hkv >= (1 << 16) || total_q * Hkv * D * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;
   const int Qt = rows / G;
   AttnArgs &a = P->args;
   a.B = B;

@@ -353,7 +353,7 @@ struct AwlPlan {
 };
 
 int plan_awl(int n_blocks, int n_pos, int vocab, AwlPlan *p) {
-  if (n_blocks < 1 || n_pos < 1 || n_pos > 63 || vocab < 1) return D3D_EINVAL;
+  if (n_blocks < 1 || n_pos < 1 || n_pos > 63 || vocab < 1 || vocab > kMaxVocab) return D3D_EINVAL;
   const long long rows = 2ll * n_blocks * n_pos;
   if (rows > INT_MAX) return D3D_EINVAL;
   int chunks = static_cast<int>(std::max<long long>(1, kAwlSlots / rows));

@@ -110,6 +110,7 @@ extern "C" int kv_commit(d3d_dtype dtype, const void *k_new, const void *v_new, 
   if (n_req < 1 || block_size < 1 || block_size > kThreads || page_size < 1 || max_pages < 1 || num_pages < 1 ||
       n_heads_kv < 1 || head_dim < 1)
     return D3D_EINVAL;
+  if (n_heads_kv > (1 << 16) || head_dim > (1 << 16)) return D3D_EUNSUPPORTED;  // keeps the row size below in range
   const long long row_bytes = static_cast<long long>(n_heads_kv) * head_dim * (dtype == D3D_BF16 ? 2 : 4);
   if (row_bytes % 16 != 0 || row_bytes > (1ll << 30)) return D3D_EUNSUPPORTED;
   CommitArgs a;

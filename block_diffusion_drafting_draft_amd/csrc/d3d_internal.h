@@ -15,6 +15,11 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
+// Largest vocabulary a logit row may have: the planners' chunk arithmetic stays inside int.
+constexpr int kMaxVocab = 1 << 28;
+// Longest request prefix draft attention takes: key positions and split lengths stay inside int.
+constexpr int kMaxPrefix = 1 << 30;
+
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies; workgroups round-robin across them
 
 // bf16 <-> f32 (bf16 is the upper half of an IEEE binary32 value).

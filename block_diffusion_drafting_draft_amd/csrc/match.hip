@@ -35,7 +35,7 @@ extern "C" int branch_cache_match(const d3d_block_desc *descs, int total_blocks,
   if (!descs || !req_block_off || !n_accepted || !next_token || !hit_branch) return D3D_EINVAL;
   if (n_req < 1 || total_blocks < 1) return D3D_EINVAL;
   const int per_block = 4;  // requests (wavefronts) per workgroup
-  d3d::match_kernel<<<(n_req + per_block - 1) / per_block, 64 * per_block, 0, stream>>>(
+  d3d::match_kernel<<<n_req / per_block + (n_req % per_block != 0), 64 * per_block, 0, stream>>>(
       descs, total_blocks, req_block_off, n_req, n_accepted, next_token, hit_branch);
   return d3d::launch_status();
 }
@@ -65,7 +65,7 @@ extern "C" int d3d_build_branch_descs_batch(int n_req, int block_size, int cover
   if (n_req < 1 || !prefix_len || !cur_anchor || !alt_anchors || !out || !req_block_off) return D3D_EINVAL;
   if (block_size < 1 || block_size > 64 || coverage < 2 || coverage > block_size || fanout < 1) return D3D_EINVAL;
   const long long per = static_cast<long long>(coverage - 1) * fanout + 2;
-  if (per * n_req > cap) return D3D_EINVAL;
+  if (cap < 1 || per > cap || n_req > cap / per) return D3D_EINVAL;  // per * n_req > cap, without overflow
   for (int i = 0; i < n_req; ++i)
     if (prefix_len[i] < 0) return D3D_EINVAL;
   const int na = static_cast<int>(per - 1);  // anchors per request

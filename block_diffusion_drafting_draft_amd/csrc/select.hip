@@ -257,7 +257,7 @@ struct SelPlan {
 };
 
 int plan_select(int n_rows, int vocab, int k, SelPlan *p) {
-  if (n_rows < 1 || vocab < 1 || k < 1 || k > kSelMaxK) return D3D_EINVAL;
+  if (n_rows < 1 || vocab < 1 || vocab > kMaxVocab || k < 1 || k > kSelMaxK) return D3D_EINVAL;
   int chunks = std::max(1, kSelSlots / n_rows);
   chunks = std::min(chunks, (vocab + kSelMinChunk - 1) / kSelMinChunk);
   chunks = std::min(chunks, kSelMaxChunks);

@@ -697,7 +697,7 @@ int check_train(d3d_dtype dtype, int L, int n_blocks, int B, int Hq, int Hkv, in
   if ((static_cast<long long>(n_blocks) * B + kQTRows / G) / (kQTRows / G) + 1 > kMaxList) return D3D_EUNSUPPORTED;
   const long long N = static_cast<long long>(L) + static_cast<long long>(n_blocks) * B;
   if (N < 1) return D3D_EINVAL;
-  if (N * Hq * kTD * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;  // 32-bit buffer offsets
+  if (N >= (1ll << 31) || Hq >= (1 << 16) || N * Hq * kTD * 2 >= (1ll << 31)) return D3D_EUNSUPPORTED;  // 32-bit buffer offsets
   sh->N = static_cast<int>(N);
   sh->G = G;
   sh->n_qitems = static_cast<int>((N + kQRows / G - 1) / (kQRows / G));

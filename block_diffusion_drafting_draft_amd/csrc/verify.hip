@@ -758,7 +758,7 @@ struct VerifyPlan {
 };
 
 int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
-  if (n_req < 1 || n_draft < 1 || n_draft > 63 || vocab < 1) return D3D_EINVAL;
+  if (n_req < 1 || n_draft < 1 || n_draft > 63 || vocab < 1 || vocab > kMaxVocab) return D3D_EINVAL;
   const int rows_req = 2 * n_draft + 1;
   const long long rows = static_cast<long long>(n_req) * rows_req;
   if (rows > INT_MAX) return D3D_EINVAL;
@@ -820,18 +820,27 @@ extern "C" size_t spec_verify_workspace(int n_req, int n_draft, int vocab) {
 
 namespace d3d {
 namespace {
+// Every argument check of a verify call, before anything touches the device; fills the plan.
+int check_verify(d3d_dtype dtype, const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
+                 int n_req, int n_draft, int vocab, float temperature, const int32_t *n_accepted,
+                 const int32_t *next_token, VerifyPlan *p) {
+  if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
+  if (!target_logits || !draft_tokens || !n_accepted || !next_token) return D3D_EINVAL;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return D3D_EINVAL;
+  if (temperature != 0.f && !draft_logits) return D3D_EINVAL;
+  return plan_verify(n_req, n_draft, vocab, p);
+}
+
 int verify_impl(d3d_dtype dtype, const void *target_logits, const void *draft_logits, const int32_t *draft_tokens,
                 int n_req, int n_draft, int vocab, float temperature, uint64_t seed, uint32_t round,
                 int32_t *n_accepted, int32_t *next_token, float *alpha, float *survival, float *tau, uint32_t *flags,
                 void *ws, size_t ws_bytes, const d3d_block_desc *descs, int total_blocks,
                 const int32_t *req_block_off, int32_t *hit, hipStream_t stream) {
-  if (dtype != D3D_BF16 && dtype != D3D_F32) return D3D_EINVAL;
-  if (!target_logits || !draft_tokens || !n_accepted || !next_token) return D3D_EINVAL;
-  if (!(temperature >= 0.f) || !isfinite(temperature)) return D3D_EINVAL;
-  const bool greedy = temperature == 0.f;
-  if (!greedy && !draft_logits) return D3D_EINVAL;
   VerifyPlan p;
-  if (plan_verify(n_req, n_draft, vocab, &p) != D3D_OK) return D3D_EINVAL;
+  if (check_verify(dtype, target_logits, draft_logits, draft_tokens, n_req, n_draft, vocab, temperature, n_accepted,
+                   next_token, &p) != D3D_OK)
+    return D3D_EINVAL;
+  const bool greedy = temperature == 0.f;
   if (!ws || ws_bytes < p.total) return D3D_EWORKSPACE;
   char *w = static_cast<char *>(ws);
   VerifyArgs a;
@@ -944,8 +953,10 @@ extern "C" int spec_verify_noalloc(d3d_dtype dtype, const void *target_logits, c
                                    int32_t *next_token, float *alpha, float *survival, float *tau,
                                    uint32_t *flags, hipStream_t stream) {
   d3d::VerifyPlan p;
-  if (d3d::plan_verify(n_req, n_draft, vocab, &p) != D3D_OK) return D3D_EINVAL;
-  if (p.total > D3D_VERIFY_SCRATCH_BYTES) return D3D_ESCRATCH;  // checked before anything else runs
+  if (d3d::check_verify(dtype, target_logits, draft_logits, draft_tokens, n_req, n_draft, vocab, temperature,
+                        n_accepted, next_token, &p) != D3D_OK)
+    return D3D_EINVAL;
+  if (p.total > D3D_VERIFY_SCRATCH_BYTES) return D3D_ESCRATCH;  // before the scratch address is looked up
   void *ws = nullptr;
   const int st = d3d::scratch_ptr(&ws);
   if (st != D3D_OK) return st;

@@ -17,6 +17,7 @@
  *    ABI. The library is thread-safe; two calls that share a workspace must not overlap in time.
  *    Its only global state is the static scratch of spec_verify_noalloc (one array per GPU, and
  *    the cached device address of that array).
+ *  - A vocabulary size (vocab) is at most 2^28; larger values are argument errors.
  *  - Device-side contents (descriptors, page tables, token ids) are not validated on the host;
  *    kernels clamp every index they derive from them so that no access leaves its buffer.
  */
@@ -40,7 +41,16 @@ enum {
   D3D_ESCRATCH = -5      /* spec_verify_noalloc: the call needs more than D3D_VERIFY_SCRATCH_BYTES */
 };
 
-typedef enum { D3D_BF16 = 0, D3D_F32 = 1 } d3d_dtype;
+/* Element type of the tensor arguments. Only D3D_BF16 and D3D_F32 are valid; the two range
+ * enumerators make every 32-bit value a value of the type, so that any other number a caller
+ * passes (from C, or through a foreign-function interface) is refused with D3D_EINVAL rather than
+ * being undefined in the library's C++. */
+typedef enum {
+  D3D_BF16 = 0,
+  D3D_F32 = 1,
+  D3D_DTYPE_RANGE_MIN_ = INT32_MIN,
+  D3D_DTYPE_RANGE_MAX_ = INT32_MAX
+} d3d_dtype;
 
 /* flags bit of a block descriptor: the block is causal inside itself (else bidirectional). */
 #define D3D_BLOCK_CAUSAL 1u
@@ -113,7 +123,7 @@ int d3d_build_branch_descs_batch(int n_req, int block_size, int coverage, int fa
  *  descs  [total_blocks] device descriptors (rej_pos and flags are used; rej_pos is clamped to
  *         [0, B]).
  *  req_block_off (host) [n_req+1], non-decreasing, req_block_off[0] == 0.
- *  req_prefix_len (host) [n_req], >= 0.
+ *  req_prefix_len (host) [n_req], in [0, 2^30].
  *  dtype  D3D_BF16 (fp32 accumulation, bf16 output) or D3D_F32 (fp32 throughout).
  *  head_dim in {64, 128}; n_heads_q / n_heads_kv in {1, 2, 4, 8, 16}; 1 <= B <= 64;
  *  1 <= n_req <= D3D_ATTN_MAX_REQ.
