@@ -7,7 +7,7 @@ A step is one pass of the whole hot path over one synthetic round of the async w
   1. branch descriptors of every request built on the host (one batched call) into pinned memory and
      copied to the GPU,
   2. draft_attn_packed (one drafter attention layer, all heads),
-  3. spec_verify (stats, decide + lse, residual / bonus mass, pick),
+  3. spec_verify (stats; decide, split residual sums and the draw in one launch),
   4. branch_cache_match.
 Inputs are resident in HBM before the timed region. The device part of a step (2-4) is captured
 once in a HIP graph, with 2 and 3 on two streams (they are independent within a round: drafting the

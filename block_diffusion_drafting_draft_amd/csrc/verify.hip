@@ -13,17 +13,25 @@
 //              logit of the slice with fp32 exp2 per element and fp64 accumulation per thread (the
 //              maximum and first argmax when greedy), and the logit at the row's draft token when
 //              the slice holds it. Partial per (row, chunk).
-//   2. decide + lse   grid (sample chunk, request): every workgroup stages its request's partials
-//              in LDS, merges each row in fp64, forms alpha_j from fp64 scalars, draws the Philox
+//   2. sample  grid (sample chunk, request): every workgroup stages its request's partials in
+//              LDS, merges each row in fp64, forms alpha_j from fp64 scalars, draws the Philox
 //              uniforms, finds the first rejection, S(k) and tau (the chunk-0 workgroup stores
-//              them); then the fp64 sum of exp((z - max)/T) over its 2048-token slice of the one or
-//              two rows the draw needs (target row j*, and draft row j* after a rejection).
-//   3. mass    grid (sample chunk, request): fp64 residual (or bonus) mass of each slice.
-//   4. pick    one workgroup per request: prefix over the slice masses, then a workgroup scan
-//              inside the slice that holds u'Z, returning the smallest token whose inclusive
-//              cumulative mass exceeds u'Z.
-// The sample passes read 8 consecutive tokens per thread with one 16-byte load per row.
-// Nothing returns to the host; every pass is stream-ordered after the previous one.
+//              them). Then, over its 2048-token slice of the one or two rows the draw needs
+//              (target row j*, and draft row j* after a rejection), in fp64: the slice's shares of
+//              the row sums Sp = sum exp(ap), Sq = sum exp(aq) (ap = (z^P - ref)/T, likewise aq)
+//              and the sums A, B of exp(ap), exp(aq) over the tokens with P > Q. Which tokens those
+//              are is read off ap - aq against an estimate of log(Sp/Sq) from the statistics pass;
+//              tokens within a band of it are only counted. Since Sp and Sq are common factors,
+//              the slice's residual mass is exactly A/Sp - B/Sq, so no pass has to wait for the
+//              row sums before it can weigh its tokens.
+//   3. pick    the request's last workgroup to finish its slice (an atomic count per request,
+//              zeroed by the statistics pass) forms Sp, Sq and every slice mass (a slice with
+//              tokens in the band, or every slice if the estimate missed the band, is weighed
+//              again token by token), takes the prefix over the slice masses and scans the slice
+//              that holds u'Z, returning the smallest token whose inclusive cumulative mass
+//              exceeds u'Z.
+// The sample pass reads 8 consecutive tokens per thread with one 16-byte load per row.
+// Nothing returns to the host; the sample pass is stream-ordered after the statistics pass.
 #include <float.h>
 #include <limits.h>
 #include <math.h>
@@ -47,6 +55,11 @@ constexpr int kSampleChunk = kThreads * kSampleElems;  // tokens per sample work
 constexpr int kMaxSampleChunks = 1024;
 constexpr int kMaxReqPartials = 2048;  // stats partials of one request staged in LDS by decide
 constexpr double kNear = 1e-6;
+// Half-width of the band around the estimate of log(Sp/Sq) inside which a token's side (P > Q or
+// not) is left to the exact row sums. The estimate comes from fp32 exp2 terms (per-term relative
+// error below 1.3e-6, from the argument's rounding at |x| <= 8 and the exp2 itself), so it is
+// within 2.6e-6 of the exact value; the pick checks that it is within half the band.
+constexpr double kRhoBand = 0x1p-16;
 
 struct StatPartial {
   float max;    // greedy: the chunk maximum; sampling: the chunk's reference logit (see RowAcc)
@@ -63,9 +76,20 @@ struct SampleState {
   int32_t drf_row;  // global draft row index (request * n_draft + j)
   float max_p;
   float max_q;
-  int32_t pad;
+  uint32_t near;  // flags bit 0 of the acceptance decisions
   double u;
+  double rho;  // residual draw: log(Sp/Sq) estimated from the statistics partials
 };
+
+// One (request, sample chunk) of the sample pass: the slice's shares of Sp and Sq; A and B over its
+// tokens with ap - aq above the band (A only, = sp, for the bonus draw); the count of tokens in it.
+struct SampleRec {
+  double sp, sq, a, b, amb;
+};
+constexpr int kRecFields = 5;
+// Per-request counters sit 256 bytes apart: 75 workgroups of each request increment theirs at
+// about the same time, and counters sharing a cache line serialise every request's increments.
+constexpr int kCounterStride = 64;
 
 struct VerifyArgs {
   const void *target;
@@ -86,9 +110,8 @@ struct VerifyArgs {
   float *tau;
   uint32_t *flags;
   StatPartial *stats;
-  SampleState *state;
-  double *lse_part;   // [n_req][s_chunks][2]
-  double *mass_part;  // [n_req][s_chunks]
+  SampleRec *rec;     // [n_req][s_chunks]
+  uint32_t *counter;  // [n_req * kCounterStride] sample workgroups done; zeroed by the statistics pass
   // optional cache match of the verified outcome against the round's branch descriptors
   const d3d_block_desc *descs;
   const int32_t *req_block_off;
@@ -291,7 +314,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
     out.sum = block_sum(mine, sh_d);
     out.aux = has_y ? __float_as_int(zy) : 0;
   }
-  if (threadIdx.x == 0) a.stats[static_cast<size_t>(row) * a.chunks + chunk] = out;
+  if (threadIdx.x == 0) {
+    a.stats[static_cast<size_t>(row) * a.chunks + chunk] = out;
+    // the sample pass counts its finished workgroups per request from zero
+    if (!GREEDY && chunk == 0 && row < a.n_req) a.counter[static_cast<size_t>(row) * kCounterStride] = 0u;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -415,22 +442,22 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
   }
   if (lane == 0) {
     SampleState st;
-    st.pad = 0;
     st.tgt_row = i * (nd + 1) + n_acc;
     st.drf_row = i * nd + min(n_acc, nd - 1);  // a valid row in every mode; its values unused for the bonus
     st.max_p = rr.max[n_acc];
     st.max_q = (!a.greedy && n_acc < nd) ? rr.max[nd + 1 + n_acc] : 0.f;
     st.u = philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
     st.mode = a.greedy ? kDone : (n_acc < nd ? kResidual : kBonus);
+    st.near = near ? 1u : 0u;
+    // sums relative to the same references as the draw's ap and aq
+    st.rho = st.mode == kResidual ? log(rr.sum[n_acc]) - log(rr.sum[nd + 1 + n_acc]) : 0.0;
     *sh_state = st;
     if (store) {
       a.n_acc[i] = n_acc;
       if (a.tau) a.tau[i] = static_cast<float>(1.0 + tsum);
-      if (a.flags) a.flags[i] = near ? 1u : 0u;
       if (a.greedy) {
+        if (a.flags) a.flags[i] = 0u;
         a.next_token[i] = rr.arg[n_acc] == INT_MAX ? -1 : rr.arg[n_acc];  // -1: every logit is -inf
-      } else {
-        a.state[i] = st;
       }
     }
   }
@@ -516,55 +543,24 @@ __device__ __forceinline__ void chunk_masses(const DrawRows<T> &d, int c, int V,
   for (int k = 0; k < kSampleElems; ++k) mass[k] = d.mass(zp[k], d.mode == kResidual ? zq[k] : 0.f);
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void decide_lse_kernel(const VerifyArgs a) {
-  extern __shared__ __align__(16) unsigned char dyn_lds[];
-  __shared__ ReqRows rr;
-  __shared__ SampleState sh_state;
-  __shared__ double sh_d[kWaves];
-  const int i = blockIdx.y;
-  decide_request(a, i, reinterpret_cast<StatPartial *>(dyn_lds), rr, &sh_state, blockIdx.x == 0);
+// Block-wide sums of N doubles per thread; every thread gets the totals.
+template <int N>
+__device__ __forceinline__ void block_sums(double (&v)[N], double *sh) {
+#pragma unroll
+  for (int f = 0; f < N; ++f)
+    for (int o = 32; o > 0; o >>= 1) v[f] += __shfl_xor(v[f], o);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0)
+#pragma unroll
+    for (int f = 0; f < N; ++f) sh[w * N + f] = v[f];
   __syncthreads();
-  const SampleState st = sh_state;
-  if (st.mode == kDone) return;
-  const DrawRows<T> d = draw_rows_base<T>(a, st);
-  const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
-  float zp[kSampleElems], zq[kSampleElems];
-  load8<T, VEC>(d.p, v0, a.vocab, zp);
-  load8<T, VEC>(d.q, v0, a.vocab, zq);  // the draft row is valid in every mode
-  double sp = 0.0, sq = 0.0;
 #pragma unroll
-  for (int k = 0; k < kSampleElems; ++k) {
-    sp += exp_fp64((static_cast<double>(zp[k]) - st.max_p) * a.inv_t);
-    if (st.mode == kResidual) sq += exp_fp64((static_cast<double>(zq[k]) - st.max_q) * a.inv_t);
+  for (int f = 0; f < N; ++f) {
+    double r = sh[f];
+    for (int k = 1; k < kWaves; ++k) r += sh[k * N + f];
+    v[f] = r;
   }
-  sp = block_sum(sp, sh_d);
-  sq = block_sum(sq, sh_d);
-  if (threadIdx.x == 0) {
-    double *dst = a.lse_part + (static_cast<size_t>(i) * a.s_chunks + blockIdx.x) * 2;
-    dst[0] = sp;
-    dst[1] = sq;
-  }
-}
-
-// log of the fp64 row sums from the lse partials (each thread owns up to 4 chunks).
-template <typename T>
-__device__ __forceinline__ void finish_draw_rows(const VerifyArgs &a, int i, DrawRows<T> &d, double *sh_d) {
-  constexpr int CPT = kMaxSampleChunks / kThreads;
-  const double *src = a.lse_part + static_cast<size_t>(i) * a.s_chunks * 2;
-  double sp = 0.0, sq = 0.0;
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {  // unconditional loads (clamped), then selects
-    const int c = threadIdx.x + k * kThreads;
-    const int cc = min(c, a.s_chunks - 1);
-    const double vp = src[2 * cc], vq = src[2 * cc + 1];
-    sp += c < a.s_chunks ? vp : 0.0;
-    sq += c < a.s_chunks ? vq : 0.0;
-  }
-  sp = block_sum(sp, sh_d);
-  sq = block_sum(sq, sh_d);
-  d.log_sp = log(sp);
-  d.log_sq = d.mode == kResidual ? log(sq) : 0.0;
+  __syncthreads();
 }
 
 // Block-wide exclusive prefix sum of one double per thread (256 threads); also returns the total.
@@ -649,20 +645,14 @@ __device__ __forceinline__ Found chunk_find(const DrawRows<T> &d, int c, int V, 
   return f;
 }
 
-// The draw of request i from its chunk masses: chunk prefix, the chunk holding u'Z, then the
-// in-chunk scan.
+// The draw of request i from its chunk masses (thread t holds chunks 4t..4t+3): chunk prefix, the
+// chunk holding u'Z, then the in-chunk scan.
 template <typename T, bool VEC>
 __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const SampleState &st, DrawRows<T> d,
-                                           double *sh_d, int *sh_i, double *sh_cum, Found *sh_found) {
-  constexpr int CPT = kMaxSampleChunks / kThreads;  // each thread owns 4 consecutive chunks
-  const double *mass = a.mass_part + static_cast<size_t>(i) * a.s_chunks;
+                                           const double (&mine)[kMaxSampleChunks / kThreads], double *sh_d,
+                                           int *sh_i, double *sh_cum, Found *sh_found) {
+  constexpr int CPT = kMaxSampleChunks / kThreads;
   const int c0 = threadIdx.x * CPT;
-  double mine[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const double v = mass[min(c0 + k, a.s_chunks - 1)];  // unconditional (clamped), then a select
-    mine[k] = c0 + k < a.s_chunks ? v : 0.0;
-  }
   double run = 0.0;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) run += mine[k];
@@ -708,44 +698,128 @@ __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const Samp
   if (threadIdx.x == 0) {
     if (fabs(target - f.c_v) < kNear * z || fabs(target - f.c_prev) < kNear * z) fl |= 2u;
     a.next_token[i] = f.v;
-    if (a.flags) a.flags[i] |= fl;
+    if (a.flags) a.flags[i] = st.near | fl;
   }
   return f.v;
 }
 
-// Residual (or bonus) mass of one 2048-token chunk.
+// The slice sums of one (request, sample chunk), then, in the request's last workgroup to finish,
+// the draw.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_mass_kernel(const VerifyArgs a) {
-  __shared__ double sh_d[kWaves];
-  const int i = blockIdx.y;
-  const SampleState st = a.state[i];
-  if (st.mode == kDone) return;
-  DrawRows<T> d = draw_rows_base<T>(a, st);
-  const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
-  float zp[kSampleElems], zq[kSampleElems];
-  load8<T, VEC>(d.p, v0, a.vocab, zp);  // issued before the partial sums are reduced
-  load8<T, VEC>(d.q, v0, a.vocab, zq);  // the draft row is valid in every mode
-  finish_draw_rows(a, i, d, sh_d);
-  double r = 0.0;
-#pragma unroll
-  for (int k = 0; k < kSampleElems; ++k) r += d.mass(zp[k], zq[k]);
-  r = block_sum(r, sh_d);
-  if (threadIdx.x == 0) a.mass_part[static_cast<size_t>(i) * a.s_chunks + blockIdx.x] = r;
-}
-
-// One workgroup per request: the draw from the published chunk masses.
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs a) {
-  __shared__ double sh_d[kWaves];
+__global__ __launch_bounds__(kThreads) void sample_kernel(const VerifyArgs a) {
+  constexpr int CPT = kMaxSampleChunks / kThreads;
+  extern __shared__ __align__(16) unsigned char dyn_lds[];  // decide's partials, then the pick's prefix
+  __shared__ ReqRows rr;
+  __shared__ SampleState sh_state;
+  __shared__ double sh_d[kWaves * kRecFields];
   __shared__ int sh_i[kWaves];
-  __shared__ double sh_cum[kMaxSampleChunks];
   __shared__ Found sh_found;
-  const int i = blockIdx.x;
-  const SampleState st = a.state[i];
+  __shared__ uint32_t sh_last;
+  const int i = blockIdx.y;
+  decide_request(a, i, reinterpret_cast<StatPartial *>(dyn_lds), rr, &sh_state, blockIdx.x == 0);
+  __syncthreads();
+  const SampleState st = sh_state;
   if (st.mode == kDone) return;
   DrawRows<T> d = draw_rows_base<T>(a, st);
-  finish_draw_rows(a, i, d, sh_d);
-  const int tok = draw_token<T, VEC>(a, i, st, d, sh_d, sh_i, sh_cum, &sh_found);
+  const bool residual = st.mode == kResidual;
+  {
+    const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
+    float zp[kSampleElems], zq[kSampleElems];
+    load8<T, VEC>(d.p, v0, a.vocab, zp);
+    load8<T, VEC>(d.q, v0, a.vocab, zq);  // the draft row is valid in every mode
+    double s[kRecFields] = {0.0, 0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int k = 0; k < kSampleElems; ++k) {
+      const double ap = (static_cast<double>(zp[k]) - st.max_p) * a.inv_t;
+      const double ep = exp_fp64(ap);
+      s[0] += ep;
+      if (residual) {
+        const double aq = (static_cast<double>(zq[k]) - st.max_q) * a.inv_t;
+        const double eq = exp_fp64(aq);
+        s[1] += eq;
+        if (ep > 0.0) {  // a token without target mass has no residual mass
+          const double t = (ap - aq) - st.rho;
+          if (t > kRhoBand) {
+            s[2] += ep;
+            s[3] += eq;
+          } else if (!(t < -kRhoBand)) {
+            s[4] += 1.0;
+          }
+        }
+      }
+    }
+    if (!residual) s[2] = s[0];
+    block_sums(s, sh_d);
+    // Publication of the record. Its fields are written with device-scope atomic stores, which
+    // write through to the memory every XCD shares, and the wait makes them complete before the
+    // count is incremented; the last workgroup reads them with device-scope atomic loads, which do
+    // not hit lines another XCD's L2 may hold stale. That is the ordering a release / acquire pair
+    // gives, without its writeback and invalidation of the whole L2, which only plain accesses
+    // need and which cost ~17 us over the 1200 workgroups of a 16-request serving batch.
+    if (threadIdx.x == 0) {
+      double *dst = reinterpret_cast<double *>(a.rec + static_cast<size_t>(i) * a.s_chunks + blockIdx.x);
+#pragma unroll
+      for (int f = 0; f < kRecFields; ++f) __hip_atomic_store(dst + f, s[f], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t done = __hip_atomic_fetch_add(a.counter + static_cast<size_t>(i) * kCounterStride, 1u,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh_last = done + 1 == static_cast<uint32_t>(a.s_chunks) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!sh_last) return;
+  }
+  // the request's last workgroup: every record of the request is published
+  const SampleRec *rec = a.rec + static_cast<size_t>(i) * a.s_chunks;
+  const int c0 = threadIdx.x * CPT;
+  SampleRec mine_rec[CPT];
+  double tot[2] = {0.0, 0.0};
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {  // unconditional loads (clamped), then selects
+    const double *src = reinterpret_cast<const double *>(rec + min(c0 + k, a.s_chunks - 1));
+    double f[kRecFields];
+#pragma unroll
+    for (int q = 0; q < kRecFields; ++q) f[q] = __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mine_rec[k] = SampleRec{f[0], f[1], f[2], f[3], f[4]};
+    if (c0 + k >= a.s_chunks) mine_rec[k] = SampleRec{0.0, 0.0, 0.0, 0.0, 0.0};
+    tot[0] += mine_rec[k].sp;
+    tot[1] += mine_rec[k].sq;
+  }
+  block_sums(tot, sh_d);
+  d.log_sp = log(tot[0]);
+  d.log_sq = residual ? log(tot[1]) : 0.0;
+  const double inv_sp = 1.0 / tot[0], inv_sq = residual ? 1.0 / tot[1] : 0.0;
+  // the estimate must be within half the band for the split sums to hold
+  const bool split_ok = !residual || fabs((d.log_sp - d.log_sq) - st.rho) <= 0.5 * kRhoBand;
+  double mine[CPT];
+  bool redo[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const SampleRec &r = mine_rec[k];
+    mine[k] = residual ? fmax(0.0, r.a * inv_sp - r.b * inv_sq) : r.a * inv_sp;
+    redo[k] = c0 + k < a.s_chunks && residual && (!split_ok || r.amb > 0.0);
+  }
+  // slices whose split is not settled: weighed token by token, one slice at a time
+  for (;;) {
+    int cand = INT_MAX;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      if (redo[k]) cand = min(cand, c0 + k);
+    const int cf = block_min_int(cand, sh_i);
+    if (cf == INT_MAX) break;
+    double m[kSampleElems];
+    chunk_masses<T, VEC>(d, cf, a.vocab, m);
+    double t[1] = {0.0};
+#pragma unroll
+    for (int k = 0; k < kSampleElems; ++k) t[0] += m[k];
+    block_sums(t, sh_d);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      if (c0 + k == cf) {
+        mine[k] = t[0];
+        redo[k] = false;
+      }
+  }
+  const int tok = draw_token<T, VEC>(a, i, st, d, mine, sh_d, sh_i, reinterpret_cast<double *>(dyn_lds), &sh_found);
   if (a.hit && threadIdx.x < 64) match_outcome(a, i, st.tgt_row - i * (a.n_draft + 1), tok);
 }
 
@@ -754,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void sample_pick_kernel(const VerifyArgs 
 // ------------------------------------------------------------------------------------------------
 struct VerifyPlan {
   int chunks, chunk_len, s_chunks;
-  size_t off_stats, off_state, off_lse, off_mass, total;
+  size_t off_stats, off_rec, off_cnt, total;
 };
 
 int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
@@ -778,12 +852,10 @@ int plan_verify(int n_req, int n_draft, int vocab, VerifyPlan *p) {
   size_t off = 0;
   p->off_stats = off;
   off = align_up(off + sizeof(StatPartial) * static_cast<size_t>(rows) * p->chunks, 256);
-  p->off_state = off;
-  off = align_up(off + sizeof(SampleState) * static_cast<size_t>(n_req), 256);
-  p->off_lse = off;
-  off = align_up(off + sizeof(double) * 2 * static_cast<size_t>(n_req) * s_chunks, 256);
-  p->off_mass = off;
-  off = align_up(off + sizeof(double) * static_cast<size_t>(n_req) * s_chunks, 256);
+  p->off_rec = off;
+  off = align_up(off + sizeof(SampleRec) * static_cast<size_t>(n_req) * s_chunks, 256);
+  p->off_cnt = off;
+  off = align_up(off + sizeof(uint32_t) * kCounterStride * static_cast<size_t>(n_req), 256);
   p->total = off;
   return D3D_OK;
 }
@@ -798,14 +870,11 @@ int launch_verify(const VerifyArgs &a, hipStream_t stream) {
   else
     stats_kernel<T, VEC, false><<<stat_grid, kThreads, 0, stream>>>(a);
   const int rows_req = a.greedy ? a.n_draft + 1 : 2 * a.n_draft + 1;
-  const size_t lds = sizeof(StatPartial) * static_cast<size_t>(rows_req) * a.chunks;
-  const dim3 d_grid(a.greedy ? 1 : a.s_chunks, a.n_req);
-  decide_lse_kernel<T, VEC><<<d_grid, kThreads, lds, stream>>>(a);
-  if (!a.greedy) {
-    const dim3 s_grid(a.s_chunks, a.n_req);
-    sample_mass_kernel<T, VEC><<<s_grid, kThreads, 0, stream>>>(a);
-    sample_pick_kernel<T, VEC><<<a.n_req, kThreads, 0, stream>>>(a);
-  }
+  // the dynamic stage holds decide's partials, then (last workgroup) the pick's chunk prefix
+  const size_t lds = std::max(sizeof(StatPartial) * static_cast<size_t>(rows_req) * a.chunks,
+                              sizeof(double) * static_cast<size_t>(a.s_chunks));
+  const dim3 grid(a.greedy ? 1 : a.s_chunks, a.n_req);
+  sample_kernel<T, VEC><<<grid, kThreads, lds, stream>>>(a);
   return launch_status();
 }
 
@@ -866,9 +935,8 @@ int verify_impl(d3d_dtype dtype, const void *target_logits, const void *draft_lo
   a.tau = tau;
   a.flags = flags;
   a.stats = reinterpret_cast<StatPartial *>(w + p.off_stats);
-  a.state = reinterpret_cast<SampleState *>(w + p.off_state);
-  a.lse_part = reinterpret_cast<double *>(w + p.off_lse);
-  a.mass_part = reinterpret_cast<double *>(w + p.off_mass);
+  a.rec = reinterpret_cast<SampleRec *>(w + p.off_rec);
+  a.counter = reinterpret_cast<uint32_t *>(w + p.off_cnt);
   a.descs = descs;
   a.req_block_off = req_block_off;
   a.total_blocks = total_blocks;

@@ -207,10 +207,10 @@ int spec_verify(d3d_dtype dtype, const void *target_logits, const void *draft_lo
  * host threads without ordering) race and give undefined outputs. Its contents carry over from
  * call to call; none of them is read before it is written, so nothing is cleared.
  * Errors: as spec_verify; D3D_ESCRATCH (nothing launched) when spec_verify_workspace(n_req,
- * n_draft, vocab) exceeds D3D_VERIFY_SCRATCH_BYTES (e.g. about 1700 requests of B = 16 at
+ * n_draft, vocab) exceeds D3D_VERIFY_SCRATCH_BYTES (e.g. about 1650 requests of B = 16 at
  * V = 151936); D3D_EHIP if the array's device address cannot be obtained.
  * ------------------------------------------------------------------------------------------- */
-#define D3D_VERIFY_SCRATCH_BYTES ((size_t)4 << 20)
+#define D3D_VERIFY_SCRATCH_BYTES ((size_t)6 << 20)
 
 int spec_verify_noalloc(d3d_dtype dtype, const void *target_logits, const void *draft_logits,
                         const int32_t *draft_tokens, int n_req, int n_draft, int vocab, float temperature,

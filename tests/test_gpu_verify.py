@@ -39,8 +39,11 @@ def _run(zt, zd, tok, dtype, T, seed, round_):
 # reported and one above 2e-6 must not be.
 BAND_SET, BAND_CLEAR = 0.5e-6, 2e-6
 # Window of a sampled draw that fp64 on both sides may legitimately decide differently: relative to Z,
-# plus an absolute floor for the cancellation in max(0, P - Q) (both sides normalise P and Q to 1).
-SAMPLE_WINDOW_REL, SAMPLE_WINDOW_ABS = 1e-9, 1e-12
+# plus an absolute floor for the cancellation in max(0, P - Q). Both sides normalise P and Q to 1, so
+# the cumulative residual mass is off by a few ulp of 1 at most (~5e-16; the library's split sums
+# A/Sp - B/Sq lose at most an ulp of each chunk's P and Q mass, which sum to at most 2): 1e-14 keeps
+# a 20x margin and still compares draws whose total residual Z is ~1e-6.
+SAMPLE_WINDOW_REL, SAMPLE_WINDOW_ABS = 1e-9, 1e-14
 
 
 def _compare(zt, zd, tok, T, seed, round_, got, name, counts=None):
@@ -170,6 +173,54 @@ def test_fuzz(case):
     open_ = _compare(inp["z_target"], inp["z_draft"], inp["tokens"], T, w.philox_seed, 5, got, str(case))
     _check_open(open_, n_req, str(case))
     del base
+
+
+@pytest.mark.parametrize("dtype,where,delta", [("bf16", "argmax", 0.5), ("bf16", "random", 3.0),
+                                                ("f32", "balanced", 0.25)])
+def test_near_equal_rows(dtype, where, delta):
+    """Draft rows equal to the target rows except the drafted token y, raised by delta. Every other
+    token then has one common P/Q, so its side of P > Q is decided by log(Sp/Sq) alone.
+    argmax: y is the row's top token, so the residual is a small difference of two nearly equal sums
+    over every other token (the split sums' cancellation case). random: a random y, whose share
+    leaves log(Sp/Sq) near the band around the statistics pass's estimate. balanced (fp32): the row's
+    second token is lowered by exactly the mass y gains, so log(Sp/Sq) is ~1e-9 and every token is in
+    the band: each slice is weighed again token by token."""
+    require_gpu()
+    _say(f"verify: near-equal rows, {dtype} {where} token raised by {delta}")
+    rng = np.random.default_rng({"argmax": 17, "random": 18, "balanced": 19}[where])
+    n_req, B, V = 16, 16, 151936
+    zt = rng.normal(0, 2.0, size=(n_req, B, V)).astype(np.float32)
+    if dtype == "bf16":
+        zt = synth.round_bf16(zt)
+    zd = zt[:, :B - 1].copy()
+    if where == "random":
+        tok = rng.integers(0, V, size=(n_req, B - 1)).astype(np.int32)
+    else:
+        tok = np.argmax(zt[:, :B - 1], axis=-1).astype(np.int32)
+    for i in range(n_req):
+        for j in range(B - 1):
+            y = tok[i, j]
+            raised = np.array([zd[i, j, y] + delta], dtype=np.float32)
+            zd[i, j, y] = synth.round_bf16(raised)[0] if dtype == "bf16" else raised[0]
+            if where == "balanced":
+                # take the mass y gains from the next tokens down, at most half of each one's
+                owe = np.exp(np.float64(zd[i, j, y])) - np.exp(np.float64(zt[i, j, y]))
+                for w in np.argsort(zt[i, j])[::-1][1:]:
+                    have = np.exp(np.float64(zt[i, j, w]))
+                    take = min(owe, 0.5 * have)
+                    zd[i, j, w] = np.float32(np.log(have - take))
+                    owe -= take
+                    if owe <= 0.0:
+                        break
+    counts = dict(compared=0, open=0, flagged=0, total=0)
+    rejected = 0
+    for round_ in range(2):
+        got = _run(zt, zd, tok, dtype, 1.0, 0xBEEF, round_)
+        rejected += int(np.sum(got["n_accepted"] < B - 1))
+        _compare(zt, zd, tok, 1.0, 0xBEEF, round_, got, f"near-equal {dtype} {where} round {round_}", counts)
+    _say(f"  {counts}, {rejected} residual draws")
+    assert rejected >= 8, rejected
+    _check_open(counts["open"], counts["total"], "near-equal rows")
 
 
 def test_equal_distributions_accept_all_and_bonus_law():
