@@ -177,4 +177,132 @@ inline int launch_status() {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// ------------------------------------------------------------------------------------------------
+// Wavefront collectives without LDS traffic: DPP moves inside rows of 16 lanes and gfx950's
+// permlane swaps between rows. (A lane shuffle goes through ds_bpermute, an LDS round trip per
+// step; these are VALU moves.) A reduction leaves its result in every lane of the group; its
+// operation must be commutative and associative, since inside a row the partner is a mirror lane,
+// not the xor lane.
+// ------------------------------------------------------------------------------------------------
+namespace wave {
+
+// DPP controls (GFX9 encoding)
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kRowMirror = 0x140;     // lane i <-> 15 - i within 16
+constexpr int kRowShr = 0x110;        // + k: lane i takes lane i - k of its row
+constexpr int kRowBcast15 = 0x142;    // lane 15 of a row to every lane of the next row
+constexpr int kRowBcast31 = 0x143;    // lane 31 to every lane of rows 2 and 3
+constexpr int kWaveShr1 = 0x138;      // lane i takes lane i - 1 of the wavefront
+
+template <typename T>
+struct Words;
+template <>
+struct Words<float> {
+  static constexpr int N = 1;
+  __device__ static void split(float v, uint32_t (&w)[1]) { w[0] = __float_as_uint(v); }
+  __device__ static float join(const uint32_t (&w)[1]) { return __uint_as_float(w[0]); }
+};
+template <>
+struct Words<int> {
+  static constexpr int N = 1;
+  __device__ static void split(int v, uint32_t (&w)[1]) { w[0] = static_cast<uint32_t>(v); }
+  __device__ static int join(const uint32_t (&w)[1]) { return static_cast<int>(w[0]); }
+};
+template <>
+struct Words<double> {
+  static constexpr int N = 2;
+  __device__ static void split(double v, uint32_t (&w)[2]) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    w[0] = static_cast<uint32_t>(b);
+    w[1] = static_cast<uint32_t>(b >> 32);
+  }
+  __device__ static double join(const uint32_t (&w)[2]) {
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(w[1]) << 32) | w[0]));
+  }
+};
+
+// The DPP move CTRL of v; lanes without a source (or outside ROW_MASK) get `old`.
+template <int CTRL, int ROW_MASK = 0xF, typename T>
+__device__ __forceinline__ T move(T old, T v) {
+  using W = Words<T>;
+  uint32_t o[W::N], x[W::N];
+  W::split(old, o);
+  W::split(v, x);
+#pragma unroll
+  for (int k = 0; k < W::N; ++k)
+    x[k] = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(o[k]), static_cast<int>(x[k]), CTRL, ROW_MASK, 0xF, false));
+  return W::join(x);
+}
+
+// op of v over the lane pairs (i, i ^ 16) (ROWS = 16) or (i, i ^ 32) (ROWS = 32), in every lane.
+template <int ROWS, typename T, typename Op>
+__device__ __forceinline__ T swap_combine(T v, Op op) {
+  using W = Words<T>;
+  uint32_t x[W::N], a[W::N], b[W::N];
+  W::split(v, x);
+#pragma unroll
+  for (int k = 0; k < W::N; ++k) {
+    if constexpr (ROWS == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(x[k], x[k], false, false);
+      a[k] = r[0];
+      b[k] = r[1];
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(x[k], x[k], false, false);
+      a[k] = r[0];
+      b[k] = r[1];
+    }
+  }
+  return op(W::join(a), W::join(b));
+}
+
+// op over each group of G consecutive lanes (G a power of two, 1..64; uniform across the wave).
+template <typename T, typename Op>
+__device__ __forceinline__ T reduce(T v, int G, Op op) {
+  if (G > 1) v = op(v, move<kQuadXor1>(v, v));
+  if (G > 2) v = op(v, move<kQuadXor2>(v, v));
+  if (G > 4) v = op(v, move<kRowHalfMirror>(v, v));
+  if (G > 8) v = op(v, move<kRowMirror>(v, v));
+  if (G > 16) v = swap_combine<16>(v, op);
+  if (G > 32) v = swap_combine<32>(v, op);
+  return v;
+}
+
+// Inclusive scan over the 64 lanes in lane order; `id` is op's identity.
+template <typename T, typename Op>
+__device__ __forceinline__ T incl_scan(T v, T id, Op op) {
+  v = op(v, move<kRowShr + 1>(id, v));
+  v = op(v, move<kRowShr + 2>(id, v));
+  v = op(v, move<kRowShr + 4>(id, v));
+  v = op(v, move<kRowShr + 8>(id, v));
+  v = op(v, move<kRowBcast15, 0xA>(id, v));
+  v = op(v, move<kRowBcast31, 0xC>(id, v));
+  return v;
+}
+
+// The previous lane's value (lane 0: id): an inclusive scan made exclusive.
+template <typename T>
+__device__ __forceinline__ T shift_up(T v, T id) {
+  return move<kWaveShr1>(id, v);
+}
+
+struct Add {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct Mul {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a * b; }
+};
+struct Max {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct Min {
+  __device__ int operator()(int a, int b) const { return a < b ? a : b; }
+};
+
+}  // namespace wave
+
 }  // namespace d3d

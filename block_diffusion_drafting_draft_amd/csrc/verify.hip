@@ -131,7 +131,7 @@ __device__ __forceinline__ void match_outcome(const VerifyArgs &a, int i, int n_
 // block reductions (256 threads = 4 wavefronts)
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ float block_max(float v, float *sh) {
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = wave::reduce(v, 64, wave::Max{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
   __syncthreads();
@@ -142,7 +142,7 @@ __device__ __forceinline__ float block_max(float v, float *sh) {
 }
 
 __device__ __forceinline__ double block_sum(double v, double *sh) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  v = wave::reduce(v, 64, wave::Add{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
   __syncthreads();
@@ -153,7 +153,7 @@ __device__ __forceinline__ double block_sum(double v, double *sh) {
 }
 
 __device__ __forceinline__ int block_min_int(int v, int *sh) {
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  v = wave::reduce(v, 64, wave::Min{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
   __syncthreads();
@@ -327,10 +327,11 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
 // Local rows 0..nd are the request's target rows, nd+1..2nd its draft rows (greedy: target only).
 struct ReqRows {
   float max[127];
-  double sum[127];
+  double logsum[127];  // log of the row's sum of exp((z - max) / T)
+  double lp[127];      // log-probability of the row's draft token (rows with one)
   int arg[127];
-  float zy[127];  // logit at the row's draft token (rows with one)
   int tok[63];
+  double u[64];        // the request's uniforms: u_j (j < n_draft), u' (j = n_draft)
 };
 
 // Loads the request's stats partials into LDS (one round trip), merges every row with a group of
@@ -359,6 +360,11 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
     }
     if (threadIdx.x < nd)
       rr.tok[threadIdx.x] = min(max(a.tokens[static_cast<size_t>(i) * nd + threadIdx.x], 0), a.vocab - 1);
+    // the request's Philox uniforms, drawn while the partials are in flight (they depend on no
+    // logit): lane j < n_draft draws u_j, lane n_draft draws u'
+    if (!a.greedy && threadIdx.x <= nd)
+      rr.u[threadIdx.x] = threadIdx.x < nd ? philox_uniform(a.seed, threadIdx.x, static_cast<uint32_t>(i), a.round, 0u)
+                                           : philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
     u32x4 *dst = reinterpret_cast<u32x4 *>(part);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -383,10 +389,8 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
       }
     }
   }
-  float wm = m;
-  for (int o = g >> 1; o > 0; o >>= 1) wm = fmaxf(wm, __shfl_xor(wm, o));
-  int warg = m == wm ? arg : INT_MAX;
-  for (int o = g >> 1; o > 0; o >>= 1) warg = min(warg, __shfl_xor(warg, o));
+  const float wm = wave::reduce(m, g, wave::Max{});
+  const int warg = wave::reduce(m == wm ? arg : INT_MAX, g, wave::Min{});
   double ws = 0.0;
   if (!a.greedy && r < n_rows && wm != -INFINITY) {
     for (int c = sub; c < C; c += g) {
@@ -394,15 +398,20 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
       if (q.max != -INFINITY) ws += q.sum * exp_fp64((static_cast<double>(q.max) - wm) * a.inv_t);
     }
   }
-  for (int o = g >> 1; o > 0; o >>= 1) ws += __shfl_xor(ws, o);
+  ws = wave::reduce(ws, g, wave::Add{});
   if (sub == 0 && r < n_rows) {
     rr.max[r] = wm;
-    rr.sum[r] = ws;
     rr.arg[r] = warg;
-    const int j = r <= nd ? r : r - nd - 1;
-    if (!a.greedy && j < nd) {
-      const int y = rr.tok[j];
-      rr.zy[r] = __int_as_float(part[r * C + y / a.chunk_len].aux);
+    if (!a.greedy) {
+      // per row, in parallel: the log of the row sum and the draft token's log-probability
+      // log P_j(y) = (z_y - ref)/T - log sum_j, so the decision needs no exp, division or log
+      const double ls = log(ws);
+      rr.logsum[r] = ls;
+      const int j = r <= nd ? r : r - nd - 1;
+      if (j < nd) {
+        const float zy = __int_as_float(part[r * C + rr.tok[j] / a.chunk_len].aux);
+        rr.lp[r] = wm == -INFINITY ? -INFINITY : (static_cast<double>(zy) - wm) * a.inv_t - ls;
+      }
     }
   }
   __syncthreads();
@@ -416,26 +425,20 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
       // a row of -inf logits has no argmax (INT_MAX): its draft is rejected
       alpha = (rr.tok[j] == rr.arg[j]) ? 1.0 : 0.0;
     } else {
-      // P_j(y) = exp((z_y - ref)/T) / sum_j, likewise Q_j(y)
-      const double py = exp_fp64((static_cast<double>(rr.zy[j]) - rr.max[j]) * a.inv_t) / rr.sum[j];
-      const double qy =
-          exp_fp64((static_cast<double>(rr.zy[nd + 1 + j]) - rr.max[nd + 1 + j]) * a.inv_t) / rr.sum[nd + 1 + j];
-      alpha = qy > 0.0 ? fmin(1.0, py / qy) : 1.0;
+      // alpha = min(1, P/Q) = min(1, exp(log P - log Q)); 1 when Q(y) is zero in fp64 (its
+      // log-probability below ln 2^-1075, where exp rounds to zero)
+      const double lq = rr.lp[nd + 1 + j];
+      alpha = lq > -745.1332191019412 ? fmin(1.0, exp_fp64(rr.lp[j] - lq)) : 1.0;
     }
-    u = philox_uniform(a.seed, static_cast<uint32_t>(j), static_cast<uint32_t>(i), a.round, 0u);
+    u = a.greedy ? 0.5 : rr.u[j];  // greedy: alpha is 0 or 1, any u in (0, 1) decides it
   }
   // first rejection: lowest lane with !(u < alpha)
   const unsigned long long rej = __ballot(j < nd && !(u < alpha));
   const int n_acc = rej ? __ffsll(static_cast<long long>(rej)) - 1 : nd;
   const unsigned long long near = __ballot(!a.greedy && j < nd && j <= n_acc && fabs(u - alpha) < kNear);
   // S(k) = prod_{j<k} alpha_j: inclusive prefix product over lanes
-  double surv = alpha;  // lanes >= nd hold 1
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(surv, o);
-    if (lane >= o) surv *= t;
-  }
-  double tsum = j < nd ? surv : 0.0;
-  for (int o = 32; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o);
+  const double surv = wave::incl_scan(alpha, 1.0, wave::Mul{});  // lanes >= nd hold 1
+  const double tsum = wave::reduce(j < nd ? surv : 0.0, 64, wave::Add{});
   if (store && j < nd) {
     if (a.alpha) a.alpha[static_cast<size_t>(i) * nd + j] = static_cast<float>(alpha);
     if (a.survival) a.survival[static_cast<size_t>(i) * nd + j] = static_cast<float>(surv);
@@ -446,11 +449,11 @@ __device__ __forceinline__ void decide_request(const VerifyArgs &a, int i, StatP
     st.drf_row = i * nd + min(n_acc, nd - 1);  // a valid row in every mode; its values unused for the bonus
     st.max_p = rr.max[n_acc];
     st.max_q = (!a.greedy && n_acc < nd) ? rr.max[nd + 1 + n_acc] : 0.f;
-    st.u = philox_uniform(a.seed, 0u, static_cast<uint32_t>(i), a.round, 1u);
+    st.u = a.greedy ? 0.0 : rr.u[nd];
     st.mode = a.greedy ? kDone : (n_acc < nd ? kResidual : kBonus);
     st.near = near ? 1u : 0u;
     // sums relative to the same references as the draw's ap and aq
-    st.rho = st.mode == kResidual ? log(rr.sum[n_acc]) - log(rr.sum[nd + 1 + n_acc]) : 0.0;
+    st.rho = st.mode == kResidual ? rr.logsum[n_acc] - rr.logsum[nd + 1 + n_acc] : 0.0;
     *sh_state = st;
     if (store) {
       a.n_acc[i] = n_acc;
@@ -547,8 +550,7 @@ __device__ __forceinline__ void chunk_masses(const DrawRows<T> &d, int c, int V,
 template <int N>
 __device__ __forceinline__ void block_sums(double (&v)[N], double *sh) {
 #pragma unroll
-  for (int f = 0; f < N; ++f)
-    for (int o = 32; o > 0; o >>= 1) v[f] += __shfl_xor(v[f], o);
+  for (int f = 0; f < N; ++f) v[f] = wave::reduce(v[f], 64, wave::Add{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0)
 #pragma unroll
@@ -565,24 +567,18 @@ __device__ __forceinline__ void block_sums(double (&v)[N], double *sh) {
 
 // Block-wide exclusive prefix sum of one double per thread (256 threads); also returns the total.
 __device__ __forceinline__ double block_excl_scan(double v, double *sh, double *total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double incl = v;
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) sh[wave] = incl;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const double incl = wave::incl_scan(v, 0.0, wave::Add{});
+  if (lane == 63) sh[wv] = incl;
   __syncthreads();
   double off = 0.0, tot = 0.0;
   for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) off += sh[w];
+    if (w < wv) off += sh[w];
     tot += sh[w];
   }
   __syncthreads();
-  double excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = 0.0;
   *total = tot;
-  return off + excl;
+  return off + wave::shift_up(incl, 0.0);
 }
 
 // Inside sample chunk c, whose tokens start at cumulative mass `offset`: the smallest v with
