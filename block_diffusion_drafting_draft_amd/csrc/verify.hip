@@ -565,6 +565,28 @@ __device__ __forceinline__ void block_sums(double (&v)[N], double *sh) {
   __syncthreads();
 }
 
+// A workgroup-uniform copy of the state read from LDS, held in scalar registers.
+__device__ __forceinline__ int32_t sgpr(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float sgpr(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+__device__ __forceinline__ double sgpr(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(b));
+  const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+__device__ __forceinline__ SampleState uniform_state(const SampleState &s) {
+  SampleState u;
+  u.mode = sgpr(s.mode);
+  u.tgt_row = sgpr(s.tgt_row);
+  u.drf_row = sgpr(s.drf_row);
+  u.max_p = sgpr(s.max_p);
+  u.max_q = sgpr(s.max_q);
+  u.near = static_cast<uint32_t>(sgpr(static_cast<int32_t>(s.near)));
+  u.u = sgpr(s.u);
+  u.rho = sgpr(s.rho);
+  return u;
+}
+
 // Block-wide exclusive prefix sum of one double per thread (256 threads); also returns the total.
 __device__ __forceinline__ double block_excl_scan(double v, double *sh, double *total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -654,6 +676,7 @@ __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const Samp
   for (int k = 0; k < CPT; ++k) run += mine[k];
   double z;
   double base = block_excl_scan(run, sh_d, &z);
+  z = sgpr(z);
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     base += mine[k];
@@ -679,7 +702,7 @@ __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const Samp
     z = zp_tot;
     __syncthreads();
   }
-  const double target = st.u * z;
+  const double target = sgpr(st.u * z);
   int cand = INT_MAX, lastpos = -1;
   for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
     const double below = c > 0 ? sh_cum[c - 1] : 0.0;
@@ -688,8 +711,8 @@ __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const Samp
   }
   const int c_star = block_min_int(cand, sh_i);
   const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
-  const int c = c_star != INT_MAX ? c_star : max(c_last, 0);
-  const double offset = c > 0 ? sh_cum[c - 1] : 0.0;
+  const int c = sgpr(c_star != INT_MAX ? c_star : max(c_last, 0));
+  const double offset = sgpr(c > 0 ? sh_cum[c - 1] : 0.0);
   const Found f = chunk_find<T, VEC>(d, c, a.vocab, offset, target, sh_d, sh_i, sh_found);
   if (threadIdx.x == 0) {
     if (fabs(target - f.c_v) < kNear * z || fabs(target - f.c_prev) < kNear * z) fl |= 2u;
@@ -701,8 +724,11 @@ __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const Samp
 
 // The slice sums of one (request, sample chunk), then, in the request's last workgroup to finish,
 // the draw.
+// At most 80 VGPRs (6 waves per SIMD): the draft attention kernel that runs beside verify in a round
+// leaves 80 per SIMD on each of its compute units, so a sample workgroup fits next to it instead of
+// holding a compute unit that an attention workgroup then waits for.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_kernel(const VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void sample_kernel(const VerifyArgs a) {
   constexpr int CPT = kMaxSampleChunks / kThreads;
   extern __shared__ __align__(16) unsigned char dyn_lds[];  // decide's partials, then the pick's prefix
   __shared__ ReqRows rr;
@@ -714,7 +740,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(const VerifyArgs a) {
   const int i = blockIdx.y;
   decide_request(a, i, reinterpret_cast<StatPartial *>(dyn_lds), rr, &sh_state, blockIdx.x == 0);
   __syncthreads();
-  const SampleState st = sh_state;
+  const SampleState st = uniform_state(sh_state);  // in scalar registers: the budget is 80 VGPRs
   if (st.mode == kDone) return;
   DrawRows<T> d = draw_rows_base<T>(a, st);
   const bool residual = st.mode == kResidual;
@@ -724,13 +750,15 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(const VerifyArgs a) {
     load8<T, VEC>(d.p, v0, a.vocab, zp);
     load8<T, VEC>(d.q, v0, a.vocab, zq);  // the draft row is valid in every mode
     double s[kRecFields] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    // the references as fp64 in scalar registers (converted per use they took vector registers)
+    const double ref_p = sgpr(static_cast<double>(st.max_p)), ref_q = sgpr(static_cast<double>(st.max_q));
 #pragma unroll
     for (int k = 0; k < kSampleElems; ++k) {
-      const double ap = (static_cast<double>(zp[k]) - st.max_p) * a.inv_t;
+      const double ap = (static_cast<double>(zp[k]) - ref_p) * a.inv_t;
       const double ep = exp_fp64(ap);
       s[0] += ep;
       if (residual) {
-        const double aq = (static_cast<double>(zq[k]) - st.max_q) * a.inv_t;
+        const double aq = (static_cast<double>(zq[k]) - ref_q) * a.inv_t;
         const double eq = exp_fp64(aq);
         s[1] += eq;
         if (ep > 0.0) {  // a token without target mass has no residual mass
@@ -767,32 +795,32 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(const VerifyArgs a) {
   // the request's last workgroup: every record of the request is published
   const SampleRec *rec = a.rec + static_cast<size_t>(i) * a.s_chunks;
   const int c0 = threadIdx.x * CPT;
-  SampleRec mine_rec[CPT];
+  // the row sums first, then (second pass, few registers live across the reduction) each chunk's mass
+  const auto field = [&](int k, int f) {
+    const double *src = reinterpret_cast<const double *>(rec + min(c0 + k, a.s_chunks - 1));
+    return __hip_atomic_load(src + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   double tot[2] = {0.0, 0.0};
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {  // unconditional loads (clamped), then selects
-    const double *src = reinterpret_cast<const double *>(rec + min(c0 + k, a.s_chunks - 1));
-    double f[kRecFields];
-#pragma unroll
-    for (int q = 0; q < kRecFields; ++q) f[q] = __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    mine_rec[k] = SampleRec{f[0], f[1], f[2], f[3], f[4]};
-    if (c0 + k >= a.s_chunks) mine_rec[k] = SampleRec{0.0, 0.0, 0.0, 0.0, 0.0};
-    tot[0] += mine_rec[k].sp;
-    tot[1] += mine_rec[k].sq;
+    const double sp = field(k, 0), sq = field(k, 1);
+    tot[0] += c0 + k < a.s_chunks ? sp : 0.0;
+    tot[1] += c0 + k < a.s_chunks ? sq : 0.0;
   }
   block_sums(tot, sh_d);
-  d.log_sp = log(tot[0]);
-  d.log_sq = residual ? log(tot[1]) : 0.0;
-  const double inv_sp = 1.0 / tot[0], inv_sq = residual ? 1.0 / tot[1] : 0.0;
+  d.log_sp = sgpr(log(tot[0]));
+  d.log_sq = sgpr(residual ? log(tot[1]) : 0.0);
+  const double inv_sp = sgpr(1.0 / tot[0]), inv_sq = sgpr(residual ? 1.0 / tot[1] : 0.0);
   // the estimate must be within half the band for the split sums to hold
   const bool split_ok = !residual || fabs((d.log_sp - d.log_sq) - st.rho) <= 0.5 * kRhoBand;
   double mine[CPT];
   bool redo[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    const SampleRec &r = mine_rec[k];
-    mine[k] = residual ? fmax(0.0, r.a * inv_sp - r.b * inv_sq) : r.a * inv_sp;
-    redo[k] = c0 + k < a.s_chunks && residual && (!split_ok || r.amb > 0.0);
+    const double ra = field(k, 2), rb = field(k, 3), ramb = field(k, 4);
+    const bool in = c0 + k < a.s_chunks;
+    mine[k] = !in ? 0.0 : residual ? fmax(0.0, ra * inv_sp - rb * inv_sq) : ra * inv_sp;
+    redo[k] = in && residual && (!split_ok || ramb > 0.0);
   }
   // slices whose split is not settled: weighed token by token, one slice at a time
   for (;;) {
