@@ -4,15 +4,17 @@
 A step is one pass of the whole hot path over one synthetic round of the async workload
 (B = 16, C = 12, F = 2: 24 blocks, 384 packed queries; 32 query / 8 key-value heads, head dim 128,
 4096-token prefix; verify of 16 target + 15 draft rows over a 151936-token vocabulary):
-  1. branch descriptors of every request built on the host (one batched call) into pinned memory and
-     copied to the GPU,
+  1. branch descriptors of every request built on the GPU (d3d_build_branch_descs_device) from the
+     device-resident prefix lengths and anchors (in a serving loop the anchors come from draft_topk
+     on the GPU and the prefix lengths from kv_commit),
   2. draft_attn_packed (one drafter attention layer, all heads),
   3. spec_verify (stats; decide, split residual sums and the draw in one launch),
   4. branch_cache_match.
-Inputs are resident in HBM before the timed region. The device part of a step (2-4) is captured
-once in a HIP graph, with 2 and 3 on two streams (they are independent within a round: drafting the
-next block's branches overlaps verifying the current block) joined before 4; each step builds its
-descriptors on the host into a ring of pinned buffers, enqueues their copy and replays the graph.
+Inputs are resident in HBM before the timed region. A step (1-4) is captured once in a HIP graph,
+with 2 and 3 on two streams (they are independent within a round: drafting the next block's branches
+overlaps verifying the current block) joined before 4; each step replays the graph. The host
+builder's CPU time and the copy a host-built batch would need are reported beside it
+(calls_us.descriptor_build_host, descriptor_copy).
 W untimed warm-up steps, then K timed steps between device synchronisations. Per-call durations
 come from HIP events recorded on the launch stream around K replays of a graph holding only that
 call. Prints one JSON line. `--call NAME` replays only that call's graph (the command to profile one
@@ -51,7 +53,8 @@ def parse():
                    help="skip the serving batch's verify measurement (warm and cold)")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the next-row measurements (token selection, KV commit, AWL, training attention)")
-    p.add_argument("--call", choices=("draft_attn_packed", "spec_verify", "branch_cache_match", "awl_loss",
+    p.add_argument("--call", choices=("round", "descriptor_build_device", "draft_attn_packed", "spec_verify",
+                                     "branch_cache_match", "awl_loss",
                                      "train_attn_fwd", "train_attn_bwd", "draft_topk_tokens", "draft_topk_anchors",
                                      "draft_sample_tokens",
                                      "kv_commit"),
@@ -115,6 +118,10 @@ class Round:
         self.off_scratch = np.zeros(self.n_req + 1, dtype=np.int32)
         self.cur_anchor = np.ascontiguousarray(self.vin["cur_anchor"], dtype=np.int32)
         self.alt_anchors = np.ascontiguousarray(self.vin["alt_anchors"], dtype=np.int32) if w.coverage else None
+        # the device builder's inputs, resident like the round's other inputs
+        self.lens_dev = torch.from_numpy(self.lens_i32.copy()).cuda()
+        self.cur_dev = torch.from_numpy(self.cur_anchor.copy()).cuda()
+        self.alt_dev = torch.from_numpy(self.alt_anchors.copy()).cuda() if w.coverage else None
         self.out = torch.empty_like(self.q)
         need = _binding.draft_attn_packed_workspace(self.q.dtype, self.off, self.lens, self.B, self.q.shape[1],
                                                     self.k_new.shape[1], self.q.shape[2])
@@ -132,6 +139,14 @@ class Round:
         self.hit = torch.empty(self.n_req, dtype=torch.int32, device="cuda")
         self.ver_out["hit_branch"] = self.hit  # the fused verify + match writes the same hit tensor
         self.round = 0
+
+    def build_descs_device(self):
+        """The round's descriptors built on the GPU (branching workloads; a workload without branches
+        has one fixed descriptor per request, uploaded once)."""
+        if self.w.coverage:
+            self.lib.d3d_build_branch_descs_device(self.B, self.w.coverage, self.w.fanout, self.lens_dev,
+                                                   self.cur_dev, self.alt_dev, out=self.descs,
+                                                   req_block_off=self.off_dev)
 
     def build_descs(self, pinned=None):
         w = self.w
@@ -244,8 +259,7 @@ def main():
         return 0
     w = synth.WORKLOADS[args.workload]
     r = Round(w)
-    ring = [torch.empty_like(r.desc_host).pin_memory() for _ in range(3)]
-    copied = [torch.cuda.Event() for _ in ring]
+    ring = [torch.empty_like(r.desc_host).pin_memory() for _ in range(3)]  # host-path copy timing only
 
     side = torch.cuda.Stream()  # default priority
     verified = torch.cuda.Event()
@@ -258,7 +272,9 @@ def main():
         # launches (spec_verify_match) and the attention stream joins the verify stream just before
         # the merge launch (draft_attn_packed_join): the round ends with that kernel. Without a merge,
         # the match kernel follows the join (a graph that ends on a bare join measured slower).
+        # The descriptors are built first, on the GPU; both streams wait for them.
         cur = torch.cuda.current_stream()
+        r.build_descs_device()
         side.wait_stream(cur)
         with torch.cuda.stream(side):
             r.verify(match=r.attn_merges)
@@ -271,13 +287,17 @@ def main():
             cur.wait_stream(side)
             r.match()
 
+    r.build_descs()  # host build + copy: the fixed descriptors of a workload without branches
+    torch.cuda.synchronize()
     for _ in range(3):  # eager warm-up (first launches, code-object loads)
-        r.build_descs()
         device_round()
     torch.cuda.synchronize()
     graphs = {}
-    for name, fn in (("round", device_round), ("draft_attn_packed", r.attention), ("spec_verify", r.verify),
-                     ("branch_cache_match", r.match)):
+    calls = [("round", device_round), ("draft_attn_packed", r.attention), ("spec_verify", r.verify),
+             ("branch_cache_match", r.match)]
+    if w.coverage:
+        calls.append(("descriptor_build_device", r.build_descs_device))
+    for name, fn in calls:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
@@ -314,11 +334,6 @@ def main():
         return 0
 
     def step(k):
-        slot = k % len(ring)
-        copied[slot].synchronize()          # the copy that last read this pinned slot has run
-        r.build_descs(ring[slot])
-        r.descs.copy_(ring[slot], non_blocking=True)
-        copied[slot].record(cur)
         graphs["round"].replay()
 
     for k in range(args.warmup):
@@ -371,6 +386,13 @@ def main():
     t_ver_cold = summary(verify_cold_us(r.lib, r.z_t, r.z_d, r.tokens, r.vin["temperature"], r.vin["philox_seed"],
                                         r.round, r.ver_ws, r.ver_out, per_replay_us, reps))
     serve = None if args.no_serve_verify else verify_serve(torch, mean_us, per_replay_us, summary, reps)
+    # the host path for comparison: CPU time of the batched host builder, and the copy of its batch
+    scratch = torch.empty_like(r.desc_host)
+    n_host = 2000
+    t_h = time.perf_counter()
+    for _ in range(n_host):
+        r.build_descs(scratch)
+    t_desc_host = (time.perf_counter() - t_h) * 1e6 / n_host
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(cur)
@@ -379,6 +401,9 @@ def main():
     e1.record(cur)
     e1.synchronize()
     t_desc = e0.elapsed_time(e1) * 1e3 / reps
+    r.build_descs()  # the copies above overwrote the device descriptors with a host batch
+    torch.cuda.synchronize()
+    t_desc_dev = mean_us(graphs["descriptor_build_device"], reps) if w.coverage else None
     attn_flops, attn_bytes, ver_bytes = r.work()
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     attn_tflops = attn_flops / (t_attn * 1e-6) / 1e12
@@ -408,14 +433,19 @@ def main():
                    "packed_queries": int(r.q.shape[0]), "heads_q": int(r.q.shape[1]),
                    "heads_kv": int(r.k_new.shape[1]), "head_dim": int(r.q.shape[2]), "vocab": w.vocab,
                    "paged": w.paged},
-        "calls_us": {"descriptor_copy": round(t_desc, 3), "draft_attn_packed": round(t_attn, 3),
+        "calls_us": {"descriptor_build_device": None if t_desc_dev is None else round(t_desc_dev, 3),
+                     "descriptor_build_host": round(t_desc_host, 3),
+                     "descriptor_copy": round(t_desc, 3), "draft_attn_packed": round(t_attn, 3),
                      "spec_verify": round(t_ver, 3), "branch_cache_match": round(t_match, 3),
                      "device_round": round(t_round, 3)},
         "calls_us_median_p10_p90": {("device_round" if n == "round" else n): [round(v[0], 3), round(v[1], 3),
                                                                               round(v[2], 3)]
                                     for n, v in stats.items()},
-        "timing": "calls_us: mean of 100 back-to-back graph replays between two HIP events on the launch "
+        "timing": "value: wall time per step over K back-to-back steps, each one replay of the round graph "
+                  "(descriptors built on the GPU inside it); "
+                  "calls_us: mean of 100 back-to-back graph replays between two HIP events on the launch "
                   "stream after 10 warm-up replays (used for the percentages and the roofline); "
+                  "descriptor_build_host: CPU time of the batched host builder per call; "
                   "calls_us_median_p10_p90: HIP events around each of 100 replays (includes each launch's "
                   "latency)",
         "attn": {"tflops": round(attn_tflops, 2), "pct_mfma_peak": round(100 * attn_tflops / peak, 2),

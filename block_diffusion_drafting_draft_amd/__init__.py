@@ -5,7 +5,7 @@ exported here are its thin Python binding with the same names. Build the library
 ``python -m block_diffusion_drafting_draft_amd.build``.
 """
 
-_BOUND = ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "draft_attn_packed_workspace", "draft_attn_packed", "draft_attn_packed_join",
+_BOUND = ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "d3d_build_branch_descs_device", "draft_attn_packed_workspace", "draft_attn_packed", "draft_attn_packed_join",
           "spec_verify_workspace", "spec_verify", "spec_verify_match", "spec_verify_noalloc", "branch_cache_match", "draft_topk_workspace", "draft_topk",
           "draft_sample_workspace", "draft_sample", "kv_commit", "awl_loss_workspace", "awl_loss",
           "train_attn_workspace", "train_attn_fwd", "train_attn_bwd")

@@ -27,6 +27,8 @@ _SIGNATURES = {
                                            _c.c_void_p, _c.c_int, _c.POINTER(_c.c_int)]),
     "d3d_build_branch_descs_batch": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _i32p, _i32p, _i32p,
                                                  _c.c_void_p, _c.c_int, _i32p]),
+    "d3d_build_branch_descs_device": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                                  _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "draft_attn_packed_workspace": (_c.c_size_t, [_c.c_int, _i32p, _i32p, _c.c_int, _c.c_int, _c.c_int,
                                                   _c.c_int, _c.c_int]),
     "draft_attn_packed": (_c.c_int, [_c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
@@ -351,6 +353,34 @@ def spec_verify_match(target_logits, draft_logits, draft_tokens, temperature, se
     the returned dict also holds hit_branch."""
     return spec_verify(target_logits, draft_logits, draft_tokens, temperature, seed, round_,
                        match=(descs, req_block_off), **kw)
+
+
+def d3d_build_branch_descs_device(block_size, coverage, fanout, prefix_len, cur_anchor, alt_anchors, out=None,
+                                  req_block_off=None, stream=None):
+    """Batched descriptor builder on the GPU. prefix_len / cur_anchor: int32 [n_req]; alt_anchors: int32
+    [n_req, (C-1)F + 1]; all GPU tensors. out: optional int32 [>= n_req ((C-1)F + 2), 4]; req_block_off:
+    optional int32 [n_req + 1]. Returns (descs, req_block_off) as GPU tensors."""
+    for t, n in ((prefix_len, "prefix_len"), (cur_anchor, "cur_anchor"), (alt_anchors, "alt_anchors")):
+        _dev(t, n)
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{n} must be a contiguous int32 tensor")
+    n_req = prefix_len.numel()
+    per = (coverage - 1) * fanout + 2
+    if cur_anchor.numel() != n_req or alt_anchors.numel() != n_req * (per - 1):
+        raise ValueError("cur_anchor / alt_anchors do not match prefix_len")
+    if out is None:
+        out = torch.empty((n_req * per, 4), dtype=torch.int32, device=prefix_len.device)
+    if req_block_off is None:
+        req_block_off = torch.empty(n_req + 1, dtype=torch.int32, device=prefix_len.device)
+    for t, n, size in ((out, "out", 4 * n_req * per), (req_block_off, "req_block_off", n_req + 1)):
+        _dev(t, n)
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < size:
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor of at least {size} entries")
+    _check(load().d3d_build_branch_descs_device(n_req, block_size, coverage, fanout, _ptr(prefix_len),
+                                                _ptr(cur_anchor), _ptr(alt_anchors), _ptr(out),
+                                                _ptr(req_block_off), _stream(stream)),
+           "d3d_build_branch_descs_device")
+    return out, req_block_off
 
 
 def branch_cache_match(descs, req_block_off, n_accepted, next_token, hit=None, stream=None):

@@ -25,8 +25,53 @@ __global__ __launch_bounds__(256) void match_kernel(const d3d_block_desc *descs,
   if (lane == 0) hit[i] = found;
 }
 
+// One thread per descriptor: request i = t / per, block b = t mod per, in the pack order of the
+// host builder ([D3D] 方法步骤详情 step 4: the current block, then the F anchors of rejection
+// positions k = 1..C-1, k-major, then the full-accept block).
+__global__ __launch_bounds__(256) void build_descs_kernel(int n_req, int B, int C, int F, const int32_t *prefix_len,
+                                                          const int32_t *cur_anchor, const int32_t *alt_anchors,
+                                                          d3d_block_desc *out, int32_t *req_block_off) {
+  const int per = (C - 1) * F + 2;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (req_block_off && t <= n_req) req_block_off[t] = t * per;
+  if (t >= n_req * per) return;
+  const int i = t / per, b = t - i * per;
+  const int32_t *alt = alt_anchors + static_cast<size_t>(i) * (per - 1);
+  d3d_block_desc d;
+  d.prefix_len = prefix_len[i];
+  if (b == 0) {
+    d.rej_pos = 0;
+    d.anchor = cur_anchor[i];
+    d.flags = static_cast<int32_t>(D3D_BLOCK_CAUSAL);
+  } else if (b < per - 1) {
+    d.rej_pos = (b - 1) / F + 1;
+    d.anchor = alt[b - 1];  // (k - 1) F + f
+    d.flags = 0;
+  } else {
+    d.rej_pos = B;
+    d.anchor = alt[(C - 1) * F];
+    d.flags = 0;
+  }
+  out[t] = d;
+}
+
 }  // namespace
 }  // namespace d3d
+
+extern "C" int d3d_build_branch_descs_device(int n_req, int block_size, int coverage, int fanout,
+                                             const int32_t *prefix_len, const int32_t *cur_anchor,
+                                             const int32_t *alt_anchors, d3d_block_desc *out,
+                                             int32_t *req_block_off, hipStream_t stream) {
+  if (n_req < 1 || !prefix_len || !cur_anchor || !alt_anchors || !out) return D3D_EINVAL;
+  if (block_size < 1 || block_size > 64 || coverage < 2 || coverage > block_size || fanout < 1) return D3D_EINVAL;
+  const long long per = static_cast<long long>(coverage - 1) * fanout + 2;
+  if (n_req > ((1ll << 31) - 257) / per) return D3D_EINVAL;  // n_req * per < 2^31 - 256: an int32 index per thread
+  const int total = static_cast<int>(per * n_req);
+  const int grid = (std::max(total, n_req + 1) + 255) / 256;
+  d3d::build_descs_kernel<<<grid, 256, 0, stream>>>(n_req, block_size, coverage, fanout, prefix_len, cur_anchor,
+                                                    alt_anchors, out, req_block_off);
+  return d3d::launch_status();
+}
 
 extern "C" int branch_cache_match(const d3d_block_desc *descs, int total_blocks,
                                   const int32_t *req_block_off, int n_req,

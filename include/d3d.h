@@ -98,6 +98,18 @@ int d3d_build_branch_descs_batch(int n_req, int block_size, int coverage, int fa
                                  const int32_t *alt_anchors, d3d_block_desc *out, int cap,
                                  int32_t *req_block_off);
 
+/* The same batch built on the device from DEVICE arrays: in a serving loop the anchors come from
+ * draft_topk on the GPU and the prefix lengths from kv_commit, so the descriptors need no round
+ * trip through the host. Request i's (C-1)F + 2 descriptors go to out[i * ((C-1)F + 2)] (DEVICE), in
+ * the order above, from prefix_len[i], cur_anchor[i] and the (C-1)F + 1 anchors at
+ * alt_anchors[i * ((C-1)F + 1)]; req_block_off (DEVICE, n_req + 1 entries) receives i ((C-1)F + 2),
+ * or is NULL. Device values are copied as they are (not validated). One launch on `stream`.
+ * Errors: D3D_EINVAL on a bad argument or n_req ((C-1)F + 2) >= 2^31 - 256 (nothing launched). */
+int d3d_build_branch_descs_device(int n_req, int block_size, int coverage, int fanout,
+                                  const int32_t *prefix_len, const int32_t *cur_anchor,
+                                  const int32_t *alt_anchors, d3d_block_desc *out,
+                                  int32_t *req_block_off, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------------------------
  * Packed draft attention -- one drafter attention layer of the packed forward ([D3D] 核心方法:
  * prefix shared and causally encoded, attention bidirectional inside a block; 方法步骤详情 step 4).

@@ -157,6 +157,22 @@ void fuzz_build_descs_batch() {
   }
 }
 
+void fuzz_build_descs_device() {
+  const int n = coin(85) ? uniform(1, 4096) : size_arg(-2, 50);
+  const int B = coin(85) ? uniform(1, 64) : size_arg(-2, 80);
+  const int C = coin(85) ? uniform(2, B > 2 ? B : 2) : size_arg(-2, 70);
+  const int F = coin(85) ? uniform(1, 8) : size_arg(-2, 8);
+  const bool n1 = coin(4), n2 = coin(4), n3 = coin(4), n4 = coin(4);
+  const int st = d3d_build_branch_descs_device(n, B, C, F, n1 ? nullptr : fake_t<int32_t>(1),
+                                               n2 ? nullptr : fake_t<int32_t>(2), n3 ? nullptr : fake_t<int32_t>(3),
+                                               n4 ? nullptr : fake_t<d3d_block_desc>(4),
+                                               coin(50) ? fake_t<int32_t>(5) : nullptr, nullptr);
+  bool valid = n >= 1 && B >= 1 && B <= 64 && C >= 2 && C <= B && F >= 1 && !n1 && !n2 && !n3 && !n4;
+  if (valid) valid = static_cast<double>(static_cast<long long>(C - 1) * F + 2) * n < 2147483392.0;
+  CHECK(valid ? launched(st) : st == D3D_EINVAL, "device descs n=%d B=%d C=%d F=%d gave %d", n, B, C, F, st);
+  if (valid) ++g_accepted;
+}
+
 // ------------------------------------------------------------------ packed draft attention
 void fuzz_attention() {
   const int n_req = coin(85) ? uniform(1, 64) : size_arg(-2, 70);
@@ -488,6 +504,7 @@ int main(int argc, char **argv) {
   for (long it = 0; it < iters; ++it) {
     fuzz_build_descs();
     fuzz_build_descs_batch();
+    fuzz_build_descs_device();
     fuzz_attention();
     fuzz_verify();
     fuzz_match();

@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for want in ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "draft_attn_packed", "draft_attn_packed_workspace",
+    for want in ("d3d_build_branch_descs", "d3d_build_branch_descs_batch", "d3d_build_branch_descs_device",
+                 "draft_attn_packed", "draft_attn_packed_workspace",
                  "spec_verify", "spec_verify_workspace", "branch_cache_match", "draft_topk", "draft_topk_workspace",
                  "draft_sample", "draft_sample_workspace",
                  "kv_commit", "awl_loss", "awl_loss_workspace", "train_attn_workspace", "train_attn_fwd",
@@ -165,3 +166,15 @@ def test_noalloc_verify_rejects_calls_beyond_its_scratch():
                                  None, None, None, None)
     assert st == -5
     assert b"scratch" in lib.d3d_status_string(st)
+
+
+def test_device_descriptor_builder_rejects_bad_arguments_before_launching():
+    """d3d_build_branch_descs_device validates on the host (the fake pointers are never used)."""
+    lib = _binding.load()
+    fake = ctypes.c_void_p(1 << 40)
+    for n_req, B, C, F in ((0, 16, 12, 2), (1, 65, 12, 2), (1, 16, 17, 2), (1, 16, 1, 2), (1, 16, 12, 0),
+                           (1 << 26, 64, 64, 1000)):
+        st = lib.d3d_build_branch_descs_device(n_req, B, C, F, fake, fake, fake, fake, None, None)
+        assert st == -1, (n_req, B, C, F, st)
+    assert lib.d3d_build_branch_descs_device(4, 16, 12, 2, None, fake, fake, fake, None, None) == -1
+    assert lib.d3d_build_branch_descs_device(4, 16, 12, 2, fake, fake, fake, None, None, None) == -1

@@ -55,6 +55,35 @@ def test_random_outcomes_match_oracle():
     assert (want[forced_hit] >= 0).all() and (want[::7] == -1).all()
 
 
+@pytest.mark.parametrize("n_req,B,C,F", [(1, 2, 2, 1), (16, 16, 12, 2), (3, 64, 64, 3), (1000, 16, 4, 5),
+                                          (7, 8, 8, 1)])
+def test_device_descriptor_builder_matches_oracle(n_req, B, C, F):
+    """d3d_build_branch_descs_device against the oracle's pack order, field by field, plus the block
+    offsets; a second call into a larger, pre-filled buffer writes exactly its own entries."""
+    require_gpu()
+    _say(f"device descriptor build: n_req {n_req}, B {B}, C {C}, F {F}")
+    rng = np.random.default_rng(n_req * 131 + B)
+    per = (C - 1) * F + 2
+    lens = rng.integers(0, 1 << 20, size=n_req).astype(np.int32)
+    cur = rng.integers(-5, 151936, size=n_req).astype(np.int32)
+    alt = rng.integers(-5, 151936, size=(n_req, per - 1)).astype(np.int32)
+    want = np.zeros((n_req * per, 4), np.int32)
+    for i in range(n_req):
+        for b, (r, anchor, causal) in enumerate(o_pack.pack_blocks(B, C, F, int(cur[i]), alt[i])):
+            want[i * per + b] = (lens[i], r, anchor, 1 if causal else 0)
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    descs, off = _binding.d3d_build_branch_descs_device(B, C, F, to(lens), to(cur), to(alt))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(descs.cpu().numpy(), want)
+    np.testing.assert_array_equal(off.cpu().numpy(), np.arange(n_req + 1, dtype=np.int32) * per)
+    big = torch.full((n_req * per + 5, 4), -7, dtype=torch.int32, device="cuda")
+    _binding.d3d_build_branch_descs_device(B, C, F, to(lens), to(cur), to(alt), out=big)
+    torch.cuda.synchronize()
+    got = big.cpu().numpy()
+    np.testing.assert_array_equal(got[:n_req * per], want)
+    assert (got[n_req * per:] == -7).all()
+
+
 def test_one_device_round_async():
     """Descriptor build -> packed attention -> verify -> match for the async workload, each against
     the oracle; the match is fed the GPU verify outcome and compared with the oracle match of the
