@@ -61,6 +61,10 @@ def parse():
                    default=None,
                    help="only replay this call's graph (warmup + steps times, nothing else on the GPU) and print "
                         "its event-timed duration: the command to profile one call's kernels alone")
+    p.add_argument("--calls-per-graph", type=int, default=1,
+                   help="with --call: capture this many back-to-back copies of the call in its graph and "
+                        "report the time per copy (a small call's own graph replay is bounded below by the "
+                        "graph launch, ~10-15 us on this system)")
     return p.parse_args()
 
 
@@ -323,6 +327,18 @@ def main():
             g = train_attn_graphs(r, torch)[0 if args.call == "train_attn_fwd" else 1]
         else:
             g = graphs[args.call]
+        n_copies = max(1, args.calls_per_graph)
+        if n_copies > 1:
+            fn = dict(calls)[args.call] if args.call in dict(calls) else None
+            if fn is None:
+                print("--calls-per-graph applies to round, descriptor_build_device, draft_attn_packed, spec_verify "
+                      "and branch_cache_match", file=sys.stderr)
+                return 2
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(n_copies):
+                    fn()
+            torch.cuda.synchronize()
         for _ in range(args.warmup):
             g.replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -332,8 +348,9 @@ def main():
             g.replay()
         e1.record(cur)
         e1.synchronize()
-        print(json.dumps({"workload": w.name, "call": args.call, "replays": args.steps,
-                          "us_per_call": round(e0.elapsed_time(e1) * 1e3 / max(args.steps, 1), 3)}), flush=True)
+        print(json.dumps({"workload": w.name, "call": args.call, "replays": args.steps, "calls_per_graph": n_copies,
+                          "us_per_call": round(e0.elapsed_time(e1) * 1e3 / max(args.steps * n_copies, 1), 3)}),
+              flush=True)
         return 0
 
     def step(k):

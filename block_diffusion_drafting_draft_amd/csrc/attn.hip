@@ -47,7 +47,7 @@ constexpr int kThreads = 256;  // fp32 kernel and the split combine
 constexpr int kRows = 128;     // query-head rows per fp32 work item
 constexpr int kBfRows = 256;   // query-head rows per bf16 work item
 constexpr int kMinSplit = 256;
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
 
 struct ReqInfo {
   int32_t q_begin;      // global packed row of the request's first query
@@ -814,6 +814,26 @@ int plan_attn(const int32_t *off, const int32_t *pre, int n_req, int B, int Hq, 
   // pipelined and its softmax is masked), so the first split gives up that many prefix keys per tail
   // tile, rounded down to whole tiles of its own.
   const int tail_keys = (B + Qt + kKeys - 1) / kKeys * kKeys * 7 / 4;
+  // A call this small (a synchronous draft: a few row items per key/value head) leaves most compute
+  // units idle at any split count the estimate above weighs, and each workgroup's fixed fill and
+  // write dominate its few tiles: cut every prefix into the shortest splits the merge takes (one
+  // tile, or more when that would exceed kMaxSplits) and give the first split only the in-pack tail.
+  double items1 = 0;
+  for (int i = 0; i < n_req; ++i) items1 += static_cast<double>(tiles[i]) * Hkv;
+  if (items1 * 8 <= slots) {
+    for (int i = 0; i < n_req; ++i) {
+      if (pre[i] == 0) {
+        splits[i] = 1;
+        len[i] = len0[i] = 0;
+        continue;
+      }
+      int l = kKeys;
+      if (1 + (pre[i] + l - 1) / l > kMaxSplits) l = ((pre[i] + kMaxSplits - 2) / (kMaxSplits - 1) + kKeys - 1) / kKeys * kKeys;
+      len0[i] = 0;
+      len[i] = l;
+      splits[i] = 1 + (pre[i] + l - 1) / l;
+    }
+  } else
   for (int i = 0; i < n_req; ++i) {
     if (pre[i] == 0) {
       splits[i] = 1;
