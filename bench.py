@@ -402,6 +402,19 @@ def main():
     reps = 100
     names = ("draft_attn_packed", "spec_verify", "branch_cache_match", "round")
     t_attn, t_ver, t_match, t_round = (mean_us(graphs[n], reps) for n in names)
+    # Device time of one call without a graph replay's launch latency: graphs of n_copy back-to-back
+    # copies of the call, per copy. A small call's own replay is bounded below by the graph launch.
+    n_copy = 10
+    in_graph = {}
+    for name, fn in (("descriptor_build_device", r.build_descs_device), ("draft_attn_packed", r.attention),
+                     ("spec_verify", r.verify), ("branch_cache_match", r.match)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_copy):
+                fn()
+        torch.cuda.synchronize()
+        in_graph[name] = mean_us(g, 30) / n_copy
+        del g
     stats = {n: summary(per_replay_us(graphs[n], reps)) for n in names}
     t_ver_cold = summary(verify_cold_us(r.lib, r.z_t, r.z_d, r.tokens, r.vin["temperature"], r.vin["philox_seed"],
                                         r.round, r.ver_ws, r.ver_out, per_replay_us, reps))
@@ -426,8 +439,8 @@ def main():
     t_desc_dev = mean_us(graphs["descriptor_build_device"], reps)
     attn_flops, attn_bytes, ver_bytes = r.work()
     peak = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
-    attn_tflops = attn_flops / (t_attn * 1e-6) / 1e12
-    ver_gbs = ver_bytes / (t_ver * 1e-6) / 1e9
+    attn_tflops = attn_flops / (in_graph["draft_attn_packed"] * 1e-6) / 1e12
+    ver_gbs = ver_bytes / (in_graph["spec_verify"] * 1e-6) / 1e9
     traffic = None
     tf = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_traffic.json")
     if os.path.exists(tf):
@@ -464,7 +477,9 @@ def main():
         "timing": "value: wall time per step over K back-to-back steps, each one replay of the round graph "
                   "(descriptors built on the GPU inside it); "
                   "calls_us: mean of 100 back-to-back graph replays between two HIP events on the launch "
-                  "stream after 10 warm-up replays (used for the percentages and the roofline); "
+                  "stream after 10 warm-up replays (each replay's launch latency included); "
+                  "calls_us_in_graph: the same over 30 replays of a graph holding 10 back-to-back copies of "
+                  "the call, per copy (the call's device time; used for the percentages and the roofline); "
                   "descriptor_build_host: CPU time of the batched host builder per call; "
                   "calls_us_median_p10_p90: HIP events around each of 100 replays (includes each launch's "
                   "latency)",
@@ -477,6 +492,7 @@ def main():
                         "pct_hbm_peak": round(100 * ver_bytes / (t_ver_cold[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
                         "protocol": "512 MiB read before each call (untimed) to flush the MALL; logits rotate "
                                     "over 3 copies; HIP events around each call; median of 100"},
+        "calls_us_in_graph": {n: round(v, 3) for n, v in in_graph.items()},
         "roofline": {"bound": "mfma", "kernel": "draft_attn_packed (attn_kernel + combine_kernel)",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic},
