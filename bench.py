@@ -535,7 +535,7 @@ def verify_cold_us(lib, zt, zd, tokens, temperature, seed, round_, ws, out, per_
 
 def verify_serve(torch, mean_us, per_replay_us, summary, reps):
     """spec_verify on the serving batch's verify (16 requests x (16 target + 15 draft rows) over
-    V = 151936, bf16: 150,720,512 bytes), the configuration the HBM bar is judged on: warm (mean of
+    V = 151936, bf16: 150,720,512 bytes), the largest verify here, against the HBM peak: warm (mean of
     back-to-back replays) and cold (MALL flushed before each call, median)."""
     from block_diffusion_drafting_draft_amd import _binding, synth
     w = synth.WORKLOADS["serve-16req-B16C12F2-paged16-V151936"]

@@ -8,7 +8,7 @@ L = sum_{r,k} I_{r,k} w_{r,k} CE(Q_{r,k}, y*_{r,k}) / (sum_{r,k} I_{r,k} w_{r,k}
 blocks r and positions k, with I the inclusion indicator (revealed positions are context only and not
 in the loss).
 
-Readings (listed in DESIGN.md, R19):
+Readings where the pages leave a step open:
 
 * Positions k = 0..n_pos-1 are a block's future tokens (block position k+1; position 0 of the block
   is the anchor, never predicted). w_0 = 1 (empty product), w_k = prod_{j<k} alpha_j -- the verify

@@ -3,8 +3,8 @@
 [D3D, 前置知识: 异步起草与缓存命中]: after verification the verified prefix grows, and when it
 starts like a pre-drafted branch that branch's remaining draft is reused (a cache hit); otherwise a
 synchronous draft round runs. [D3D, 方法步骤详情 step 4]: the packed forward that drafted the
-branches also ran the current block under prefix-shared causal encoding. Readings (listed in
-DESIGN.md, R18):
+branches also ran the current block under prefix-shared causal encoding. Readings where the
+pages leave a step open:
 
 * The verified prefix grows by the anchor and the accepted drafts (a0, d_1 .. d_{n_acc}); the
   resampled or bonus token is the next block's anchor, whose keys / values the next forward computes.

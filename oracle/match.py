@@ -4,7 +4,7 @@
 start of one of the pre-drafted branches, the branch is a cache hit and its remaining draft tokens
 are reused; otherwise ([D3D, 核心方法]) a synchronous draft round is run.
 
-Reading (listed in the design doc): the verified prefix is the accepted slice a0, y_1..y_n (n =
+Reading (the pages leave this open): the verified prefix is the accepted slice a0, y_1..y_n (n =
 n_accepted) followed by the resampled or bonus token t. The branch with rejection position r and
 anchor a assumes the slice is the first r rows of block 0 and that its anchor comes next, so it is
 a hit exactly when r = n_accepted + 1 and a = t. The first such block in pack order wins; block 0

@@ -8,7 +8,7 @@ the budget is N_async = B[(C-1)F + 2] tokens (384 at B=16, C=12, F=2).
 bidirectional. [D3D, 前置知识: 异步起草与缓存命中]: a branch is reused when the verified prefix
 equals the start of that branch.
 
-Readings (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * The "+2" is the full-accept block plus the current block itself (block 0): the branches need
   the current block's own key/value rows for the accepted slice, so they are produced in this pass.

@@ -8,7 +8,7 @@ from its published definition: J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Sha
 Random Numbers: As Easy as 1, 2, 3", SC'11, section 3 (the Philox S-box built from two
 multiply-hi/lo products per round, a Weyl-sequence key schedule, 10 rounds).
 
-Reading (listed in the design doc): key = the 64-bit seed split into (low word, high word); counter
+Reading (the pages do not fix the stream layout): key = the 64-bit seed split into (low word, high word); counter
 words = (position j, request, round, purpose) with purpose 0 = acceptance test, 1 = residual or
 bonus draw; a uniform double takes the top 27 bits of output word 0 and the top 26 bits of word 1:
 u = ((x0 >> 5) * 2**26 + (x1 >> 6)) * 2**-53, which lies on the 53-bit grid of [0, 1).

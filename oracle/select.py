@@ -4,7 +4,7 @@
 drafts continuation blocks for each of the first C-1 rejection positions with F alternative
 anchors each, plus a full-accept block. [D3D, 前置知识: 异步起草与缓存命中]: a branch is reused
 when the verified prefix starts like it. The pages do not say how the anchors or the drafted tokens
-are chosen; the readings (listed in the design doc, R3 and R17):
+are chosen; the readings taken here:
 
 * The drafted token of a masked position is the most likely token of its logits (greedy drafting,
   the pages' own evaluation setting).

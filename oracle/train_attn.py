@@ -7,7 +7,7 @@ causally once and shared as the prefix of every block, and attention inside a bl
 bidirectional. The clean response rows are computed too (they carry the autoregressive loss).
 [DScout, 方法步骤详情 step 2]: the horizon B is drawn per update from {8, 16, 24, 32}.
 
-Reading (listed in the design doc, R20): packed rows 0..L-1 are the response; block i occupies rows
+Reading (the pages leave the layout open): packed rows 0..L-1 are the response; block i occupies rows
 L + i*B .. L + i*B + B - 1 and its anchor sits at response position a_i. A response row p sees the
 response keys j <= p. A row of block i sees the response keys j < a_i (the tokens before its anchor)
 and every row of block i. No row sees another block.

@@ -11,7 +11,7 @@ Definitions followed:
 * [DScout, 前置知识: 平均接受长度 MAT] and [D3D, 前置知识: 接受长度 τ]:
   tau = 1 + sum_{k=1}^{B-1} S(k), S(k) = prod_{j<=k} a_j, counting the target's own token.
 
-Readings (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * Rows are 0-based: target row j (j = 0..B-1) and draft row j (j = 0..B-2); row j judges draft
   token y_j (rejection position k = j + 1); target row B-1 is the bonus row.

@@ -4,7 +4,7 @@ Every HIP source is compiled with the sanitizers on its host side (device code i
 and never runs here) and linked into ``host_fuzz/host_fuzz.cpp``, which drives every entry point of
 the C ABI with random and extreme arguments: the descriptor builders, the workspace planners and
 the argument checks of every launching call. Where no GPU is visible an accepted call ends at a
-launch the HIP runtime refuses, so the driver's fake device pointers are never used. A sanitizer
+launch the HIP runtime refuses, so the fuzzer's fake device pointers are never used. A sanitizer
 report, a crash or a status that breaks the header's rules fails the test; two planted mistakes
 show that the sanitizers are really on.
 """
