@@ -132,10 +132,12 @@ struct LaneRow {
   bool valid, causal;
 };
 
-// Query row `row` (0..127) of the work item's 128 query-head rows: rows are head-major, Qt queries
-// of one head after another.
+// Query row `row` of the work item's G * Qt query-head rows: rows are query-major, the G heads of one
+// query on consecutive rows (consecutive in memory too). An item with fewer than Qt queries -- a
+// synchronous draft's few queries -- so fills its first wavefronts, and wavefronts without a valid
+// row skip the tile work.
 __device__ __forceinline__ LaneRow lane_row(const AttnArgs &a, const Item &it, int row) {
-  const int head_local = row / a.Qt, qi = row - head_local * a.Qt;
+  const int qi = row / a.G, head_local = row - qi * a.G;
   LaneRow L;
   L.q_local = it.tile * a.Qt + qi;
   L.valid = L.q_local < it.R.n_q;
@@ -154,7 +156,7 @@ __device__ __forceinline__ LaneRow lane_row(const AttnArgs &a, const Item &it, i
 
 // The output row of query-head row `row` only (no descriptor read): what the final write needs.
 __device__ __forceinline__ LaneRow out_row(const AttnArgs &a, const Item &it, int row) {
-  const int head_local = row / a.Qt, qi = row - head_local * a.Qt;
+  const int qi = row / a.G, head_local = row - qi * a.G;
   LaneRow L;
   L.q_local = it.tile * a.Qt + qi;
   L.valid = L.q_local < it.R.n_q;
@@ -338,6 +340,8 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hh = lane >> 5;
   // this lane's query row (recomputed after the walk instead of held in registers)
   auto row_of = [&]() __attribute__((always_inline)) { return lane_row(a, it, wave * 32 + (lane & 31)); };
+  // a wavefront without a valid row (an item with fewer queries than Qt) only copies and waits
+  const bool live = __ballot(out_row(a, it, wave * 32 + (lane & 31)).valid) != 0;
   bf16x8 qf[D / 16];
   // Q fragments of this lane's row. They are loaded after the first tile copies are issued, and one
   // full wait (which the compiler sees: otherwise it keeps Q pending into the loop and waits there
@@ -457,7 +461,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
         issue(kpre, vpre, it.k0 + (i + 3) * kKeys);
         if (i + 4 < n_tiles) load_pages(it.k0 + (i + 4) * kKeys);
       }
-      tile1<D, false>(kcur, vcur, fa, qf, st, c, [](int) { return true; });
+      if (live) tile1<D, false>(kcur, vcur, fa, qf, st, c, [](int) { return true; });
       wait_next(i);
     };
     load_pages(it.k0);
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
     if (n_full < n_tiles) {  // ragged last tile: keys past the split's end are masked
       const int lim_hh = k1 - (it.k0 + n_full * kKeys) - 4 * hh;
       auto vis = [&](int kc) { return kc < lim_hh; };
-      switch (n_full % kStages) {
+      if (live) switch (n_full % kStages) {
         case 0: tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c, vis); break;
         case 1: tile1<D, true>(lds_k1, lds_v1, fa, qf, st, c, vis); break;
         case 2: tile1<D, true>(lds_k2, lds_v2, fa, qf, st, c, vis); break;
@@ -517,8 +521,9 @@ __global__ __launch_bounds__(kBfThreads, 2) void attn_kernel_bf16(const AttnArgs
       }
       wait_vm<0>();
       __syncthreads();
-      tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c,
-                     [&](int kc) { return tail_visible(L, sh_blk + 4 * hh, sh_pos + 4 * hh, kc); });
+      if (live)
+        tile1<D, true>(lds_k0, lds_v0, fa, qf, st, c,
+                       [&](int kc) { return tail_visible(L, sh_blk + 4 * hh, sh_pos + 4 * hh, kc); });
     }
   }
   write_result<__bf16, D>(a, it, out_row(a, it, wave * 32 + (lane & 31)), st.o, st.m, st.l);
