@@ -91,3 +91,77 @@ def backward(q, k, v, do, L, anchors, B, scale):
         dk[:, g] += float(scale) * (ds.T @ q[:, h])
         dv[:, g] += p.T @ do[:, h]
     return dq, dk, dv
+
+
+def _rows_forward(q, k, v, vis, scale, rows):
+    """o, lse of the query rows `rows` whose visibility rows are `vis` (float64 inputs)."""
+    hq = q.shape[1]
+    grp = _group(hq, k.shape[1])
+    o = np.empty((len(rows), hq, q.shape[2]))
+    lse = np.empty((len(rows), hq))
+    for h in range(hq):
+        g = h // grp
+        s = np.where(vis, (q[rows, h] @ k[:, g].T) * float(scale), -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        tot = e.sum(axis=1, keepdims=True)
+        lse[:, h] = (m + np.log(tot))[:, 0]
+        o[:, h] = (e / tot) @ v[:, g]
+    return o, lse
+
+
+def forward_rows(q, k, v, L, anchors, B, scale, rows):
+    """forward() restricted to the packed query rows `rows`: (o [R, H_q, d], lse [R, H_q]). A row's
+    softmax involves only its own scores, so this is the same definition on fewer rows (for shapes
+    where every row would be too much work)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    rows = np.asarray(rows, dtype=np.int64)
+    return _rows_forward(q, k, v, visible_mask(L, anchors, B)[rows], scale, rows)
+
+
+def backward_rows(q, k, v, do, L, anchors, B, scale, rows):
+    """dq of the packed query rows `rows` only, [R, H_q, d]: a row's dq involves only its own scores,
+    probabilities and D_r = sum_d do_r o_r."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    rows = np.asarray(rows, dtype=np.int64)
+    hq = q.shape[1]
+    grp = _group(hq, k.shape[1])
+    vis = visible_mask(L, anchors, B)[rows]
+    o, lse = _rows_forward(q, k, v, vis, scale, rows)
+    dq = np.empty((len(rows), hq, q.shape[2]))
+    for h in range(hq):
+        g = h // grp
+        s = np.where(vis, (q[rows, h] @ k[:, g].T) * float(scale), -np.inf)
+        p = np.exp(s - lse[:, h:h + 1])
+        dp = do[rows, h] @ v[:, g].T
+        dd = np.sum(do[rows, h] * o[:, h], axis=1, keepdims=True)
+        dq[:, h] = float(scale) * ((p * (dp - dd)) @ k[:, g])
+    return dq
+
+
+def backward_keys(q, k, v, do, L, anchors, B, scale, keys):
+    """(dk, dv) of the packed keys `keys` only, [K, H_kv, d]: each is a sum over the rows that see the
+    key (and the query heads of its group), with every viewer's own lse and o."""
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    keys = np.asarray(keys, dtype=np.int64)
+    hq, hkv = q.shape[1], k.shape[1]
+    grp = _group(hq, hkv)
+    mask = visible_mask(L, anchors, B)
+    dk = np.zeros((len(keys), hkv, k.shape[2]))
+    dv = np.zeros((len(keys), hkv, v.shape[2]))
+    # every viewer's o and lse once (the keys share most of their viewers)
+    seen = np.nonzero(mask[:, keys].any(axis=1))[0]
+    if len(seen) == 0:
+        return dk, dv
+    o_all, lse_all = _rows_forward(q, k, v, mask[seen], scale, seen)
+    for i, kj in enumerate(keys):
+        sel = np.nonzero(mask[seen, kj])[0]
+        viewers, o, lse = seen[sel], o_all[sel], lse_all[sel]
+        for h in range(hq):
+            g = h // grp
+            p = np.exp((q[viewers, h] @ k[kj, g]) * float(scale) - lse[:, h])
+            dp = do[viewers, h] @ v[kj, g]
+            dd = np.sum(do[viewers, h] * o[:, h], axis=1)
+            dv[i, g] += p @ do[viewers, h]
+            dk[i, g] += float(scale) * ((p * (dp - dd)) @ q[viewers, h])
+    return dk, dv

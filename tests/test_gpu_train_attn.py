@@ -119,54 +119,26 @@ def test_train_attention_training_step_shape_sampled():
     out, lse = _binding.train_attn_fwd(qd, kd, vd, an, L, B, scale=scale)
     dq, dk, dv = _binding.train_attn_bwd(qd, kd, vd, out, dod, lse, an, L, B, scale=scale)
     torch.cuda.synchronize()
-    mask = ta.visible_mask(L, anchors, B)
-    N = mask.shape[0]
-    grp = hq // hkv
-    q64, k64, v64, do64 = (x.astype(np.float64) for x in (q, k, v, do))
-
-    def row_stats(r, h):
-        g = h // grp
-        s = (k64[mask[r], g] @ q64[r, h]) * scale
-        m = s.max()
-        e = np.exp(s - m)
-        lse_r = m + np.log(e.sum())
-        o_r = (e / e.sum()) @ v64[mask[r], g]
-        return s, lse_r, o_r
-
+    N = ta.n_rows(L, nb, B)
     rng = np.random.default_rng(5)
     rows = sorted(set([0, 1, L - 1, L, L + B - 1, N - 1]) | set(int(x) for x in rng.choice(N, 40, replace=False)))
-    o_h, lse_h, dq_h = host(out), lse.cpu().numpy(), host(dq)
-    for r in rows:
-        for h in (0, hq - 1, int(rng.integers(hq))):
-            g = h // grp
-            s, lse_r, o_r = row_stats(r, h)
-            assert abs(lse_h[r, h] - lse_r) < 2e-2, (r, h)
-            assert np.abs(o_h[r, h] - o_r).max() < 2e-2, (r, h)
-            p = np.exp(s - lse_r)
-            dp = v64[mask[r], g] @ do64[r, h]
-            ds = p * (dp - do64[r, h] @ o_r)
-            want = scale * (ds @ k64[mask[r], g])
-            assert np.abs(dq_h[r, h] - want).max() <= 2e-2 * max(np.abs(want).max(), 1e-3), (r, h)
+    heads = sorted(set([0, hq - 1]) | set(int(x) for x in rng.choice(hq, 2, replace=False)))
+    want_o, want_lse = ta.forward_rows(q, k, v, L, anchors, B, scale, rows)
+    want_dq = ta.backward_rows(q, k, v, do, L, anchors, B, scale, rows)
+    o_h, lse_h, dq_h = host(out)[rows], lse.cpu().numpy()[rows], host(dq)[rows]
+    for h in heads:
+        assert np.abs(lse_h[:, h] - want_lse[:, h]).max() < 2e-2, h
+        assert np.abs(o_h[:, h] - want_o[:, h]).max() < 2e-2, h
+        for i, r in enumerate(rows):
+            w = want_dq[i, h]
+            assert np.abs(dq_h[i, h] - w).max() <= 2e-2 * max(np.abs(w).max(), 1e-3), (r, h)
     keys = list(range(L - 64, L)) + [L + b * B + j for b in (0, 5, 77, nb - 1) for j in range(B)]
-    dk_h, dv_h = host(dk), host(dv)
-    cache = {}
-    for kj in keys:
-        viewers = np.nonzero(mask[:, kj])[0]
+    want_dk, want_dv = ta.backward_keys(q, k, v, do, L, anchors, B, scale, keys)
+    dk_h, dv_h = host(dk)[keys], host(dv)[keys]
+    for i, kj in enumerate(keys):
         for g in (0, hkv - 1):
-            want_k = np.zeros(128)
-            want_v = np.zeros(128)
-            for r in viewers:
-                for h in range(g * grp, (g + 1) * grp):
-                    if (r, h) not in cache:
-                        s, lse_r, o_r = row_stats(r, h)
-                        cache[(r, h)] = (lse_r, o_r)
-                    lse_r, o_r = cache[(r, h)]
-                    p = np.exp(scale * (q64[r, h] @ k64[kj, g]) - lse_r)
-                    dp = do64[r, h] @ v64[kj, g]
-                    want_v += p * do64[r, h]
-                    want_k += scale * p * (dp - do64[r, h] @ o_r) * q64[r, h]
-            assert np.abs(dv_h[kj, g] - want_v).max() <= 2e-2 * max(np.abs(want_v).max(), 1e-3), (kj, g)
-            assert np.abs(dk_h[kj, g] - want_k).max() <= 2e-2 * max(np.abs(want_k).max(), 1e-3), (kj, g)
+            for got, want in ((dk_h[i, g], want_dk[i, g]), (dv_h[i, g], want_dv[i, g])):
+                assert np.abs(got - want).max() <= 2e-2 * max(np.abs(want).max(), 1e-3), (kj, g)
 
 
 def test_train_attention_bad_arguments():

@@ -118,3 +118,26 @@ def test_what_a_row_may_depend_on():
     v3[~keep] = rng.normal(size=v3[~keep].shape)
     o3, _ = ta.forward(q, k3, v3, L, anchors, B, 0.5)
     assert np.allclose(o3[r0:r0 + B], o[r0:r0 + B], rtol=0, atol=1e-14)
+
+
+def test_row_and_key_restrictions_match_torch():
+    """forward_rows / backward_rows / backward_keys (the oracle evaluated on some rows or keys only, for
+    shapes where every row would be too much work) against torch's autograd on the whole problem."""
+    rng = np.random.default_rng(21)
+    L, anchors, B, hq, hkv, d = 48, [5, 20, 20, 47], 8, 4, 2, 16
+    n = ta.n_rows(L, len(anchors), B)
+    q, k, v = _inputs(rng, n, hq, hkv, d)
+    do = rng.normal(size=(n, hq, d))
+    scale = d ** -0.5
+    mask = ta.visible_mask(L, anchors, B)
+    t_o, t_dq, t_dk, t_dv = _torch_sdpa(q, k, v, mask, scale, grad_out=do)
+    rows = [0, 1, 19, L - 1, L, L + 9, n - 1]
+    o, lse = ta.forward_rows(q, k, v, L, anchors, B, scale, rows)
+    assert np.allclose(o, t_o[rows], rtol=1e-12, atol=1e-12)
+    s = (q[rows[3], 1] @ k[:, 0].T) * scale
+    assert np.isclose(lse[3, 1], np.log(np.exp(s[mask[rows[3]]]).sum()), rtol=1e-13)
+    assert np.allclose(ta.backward_rows(q, k, v, do, L, anchors, B, scale, rows), t_dq[rows], rtol=1e-10, atol=1e-12)
+    keys = [0, 4, 5, 30, L - 1, L, L + 17, n - 1]
+    dk, dv = ta.backward_keys(q, k, v, do, L, anchors, B, scale, keys)
+    assert np.allclose(dk, t_dk[keys], rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv, t_dv[keys], rtol=1e-10, atol=1e-12)
