@@ -144,9 +144,9 @@ def test_workspace_sizes():
 
 
 def test_topk_workspace():
-    # rows x chunks x k candidates of 8 bytes, 256-byte aligned; chunks fill one round of 2048 workgroups
-    # (at most 32 per row, at least 1024 tokens each)
-    assert _binding.draft_topk_workspace(384, 151936, 1) == 384 * 5 * 8
+    # rows x chunks x k candidates of 8 bytes, 256-byte aligned; chunks fill 4096 workgroups (two
+    # rounds of 8 per CU; at most 32 per row, at least 1024 tokens each): 4096 // 384 = 10 per row
+    assert _binding.draft_topk_workspace(384, 151936, 1) == 384 * 10 * 8
     assert _binding.draft_topk_workspace(11, 151936, 2) % 256 == 0
     assert _binding.draft_topk_workspace(11, 151936, 2) >= 11 * 32 * 2 * 8
     assert _binding.draft_topk_workspace(1, 7, 8) == 256
