@@ -344,7 +344,9 @@ constexpr int kQTRows = 64;                                    // query-head row
 constexpr int kMaxList = 4096;                                 // listed query tiles of the block region
 constexpr int kKvNI = kQTRows * kTD * 2 / (kKThreads * 16);   // 16-byte copies per wavefront per operand
 constexpr int kKvOps = 2 * kKvNI + 2;                          // copies per wavefront per tile (+ 2 tables)
-constexpr int kWalkChunk = 96;                                 // query tiles per workgroup
+// query tiles per workgroup: at L 4096 + 128 x 16, 32/8 heads the backward measured 1066-1099 us with
+// 96, 1023-1048 with 112 or 128, 1064-1073 with 144 or 160
+constexpr int kWalkChunk = 128;
 
 struct KStage {
   char q[kQTRows * kTD * 2];
