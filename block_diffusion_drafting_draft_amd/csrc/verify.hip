@@ -39,6 +39,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "d3d_internal.h"
 
@@ -177,58 +178,71 @@ __device__ __forceinline__ int block_min_int(int v, int *sh) {
 // |x| 2^-24 ln 2 in the term, and the terms that carry the row's mass are the ones near the top.
 // (Letting x grow to ~120 before moving, at T = 0.25 on a 151936-token row, put 3e-6 into alpha.)
 // Consumers only need some reference, not the maximum.
-template <bool GREEDY>
-struct RowAcc {
+// A term is one fma and one exp2: x = z c - mc with c = log2(e)/T and mc = m c rounded to fp32. The
+// fma forms z c - mc exactly before its one rounding, so x carries the same relative error as
+// (z - m) c, and the product's rounding residual rho = m c - mc (exact, by fma) is taken back out
+// at the end: the terms are relative to the reference m - rho/c, in fp64.
+struct GreedyAcc {
   float m = -INFINITY;
-  double s = 0.0;
   int arg = INT_MAX;
-
-  template <int N>
-  __device__ __forceinline__ static float group_max(const float (&z)[N]) {
-    float vm = z[0];
-#pragma unroll
-    for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);
-    return vm;
-  }
-
-  template <int N>
-  __device__ __forceinline__ static float group_sum(const float (&z)[N], float m, float c_log2) {
-    float part = 0.f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) part += __builtin_amdgcn_exp2f((z[k] - m) * c_log2);
-    return part;
-  }
 
   // Fold N consecutive elements starting at token index `idx` (z in fp32, exact for bf16).
   template <int N>
-  __device__ __forceinline__ void fold(const float (&z)[N], int idx, float c_log2, double inv_t) {
-    if constexpr (GREEDY) {
-      const float vm = group_max(z);
-      if (vm > m) {
-        m = vm;
-        int first = N - 1;
+  __device__ __forceinline__ void fold(const float (&z)[N], int idx, float, double) {
+    float vm = z[0];
 #pragma unroll
-        for (int k = N - 1; k >= 0; --k)
-          if (z[k] == vm) first = k;
-        arg = idx + first;
-      }
-    } else {
-      if (m == -INFINITY) {  // no finite logit yet: the first finite group maximum is the reference
-        const float vm = group_max(z);
-        if (vm == -INFINITY) return;
-        m = vm;
-      }
-      float part = group_sum(z, m, c_log2);
-      if (!(part < 0x1p8f)) {  // a logit well above the reference: move it to this group's max
-        const float vm = group_max(z);
-        s *= exp_fp64((static_cast<double>(m) - vm) * inv_t);
-        m = vm;
-        part = group_sum(z, m, c_log2);
-      }
-      s += static_cast<double>(part);
+    for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);
+    if (vm > m) {
+      m = vm;
+      int first = N - 1;
+#pragma unroll
+      for (int k = N - 1; k >= 0; --k)
+        if (z[k] == vm) first = k;
+      arg = idx + first;
     }
   }
 };
+
+struct SumAcc {
+  float m = -INFINITY, mc = -INFINITY;
+  double s = 0.0;
+
+  template <int N>
+  __device__ __forceinline__ float group_sum(const float (&z)[N], float c) const {
+    float part = __builtin_amdgcn_exp2f(__builtin_fmaf(z[0], c, -mc));
+#pragma unroll
+    for (int k = 1; k < N; ++k) part += __builtin_amdgcn_exp2f(__builtin_fmaf(z[k], c, -mc));
+    return part;
+  }
+
+  // With no finite logit seen yet mc = -inf, and a group holding one makes the sum +inf or NaN, so
+  // the one test below also sets the first reference.
+  template <int N>
+  __device__ __forceinline__ void fold(const float (&z)[N], int, float c, double) {
+    float part = group_sum(z, c);
+    if (!(part < 0x1p8f)) {
+      float vm = z[0];
+#pragma unroll
+      for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);
+      if (vm == -INFINITY) return;  // no finite logit in the group, none before it either
+      const float nmc = vm * c;
+      s = m == -INFINITY ? 0.0 : s * exp_fp64((static_cast<double>(mc) - nmc) * 0.6931471805599453);
+      m = vm;
+      mc = nmc;
+      part = group_sum(z, c);
+    }
+    s += static_cast<double>(part);
+  }
+
+  // the reference the terms are taken against, in logit units (only when m is finite)
+  __device__ __forceinline__ double ref(float c) const {
+    const float rho = __builtin_fmaf(m, c, -mc);
+    return static_cast<double>(m) - static_cast<double>(rho) / static_cast<double>(c);
+  }
+};
+
+template <bool GREEDY>
+using RowAcc = typename std::conditional<GREEDY, GreedyAcc, SumAcc>::type;
 
 __device__ __forceinline__ void unpack(const u32x4 &w, float (&z)[8], const __bf16 *) {
 #pragma unroll
@@ -281,22 +295,23 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
     const u32x4 *vp = reinterpret_cast<const u32x4 *>(base + begin);
     const int nvec = (end - begin) / W;
     constexpr int U = 4;
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += kThreads * U) {
+    // steps of U vectors per thread with every load in range (no per-load test), then the rest
+    int v = threadIdx.x;
+    for (; v + (U - 1) * kThreads < nvec; v += U * kThreads) {
       u32x4 buf[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * kThreads;
-        if (v < nvec) buf[u] = vp[v];
-      }
+      for (int u = 0; u < U; ++u) buf[u] = vp[v + u * kThreads];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int v = v0 + u * kThreads;
-        if (v < nvec) {
-          float z[W];
-          unpack(buf[u], z, static_cast<const T *>(nullptr));
-          acc.fold(z, begin + v * W, a.c_log2, a.inv_t);
-        }
+        float z[W];
+        unpack(buf[u], z, static_cast<const T *>(nullptr));
+        acc.fold(z, begin + (v + u * kThreads) * W, a.c_log2, a.inv_t);
       }
+    }
+    for (; v < nvec; v += kThreads) {
+      float z[W];
+      unpack(vp[v], z, static_cast<const T *>(nullptr));
+      acc.fold(z, begin + v * W, a.c_log2, a.inv_t);
     }
   } else {
     for (int idx = begin + threadIdx.x; idx < end; idx += kThreads) {
@@ -311,8 +326,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
     out.aux = block_min_int(acc.m == m ? acc.arg : INT_MAX, sh_i);
     out.sum = 0.0;
   } else {
-    const double mine =
-        acc.m == -INFINITY ? 0.0 : acc.s * exp_fp64((static_cast<double>(acc.m) - m) * a.inv_t);
+    const double mine = acc.m == -INFINITY ? 0.0 : acc.s * exp_fp64((acc.ref(a.c_log2) - m) * a.inv_t);
     out.sum = block_sum(mine, sh_d);
     out.aux = has_y ? __float_as_int(zy) : 0;
   }
