@@ -681,13 +681,18 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
     const ReqInfo &R = a.req[i];
     if (R.n_splits > 1 && row >= R.comb_begin && row < R.comb_begin + R.n_q * a.Hq) e = i;
   }
+  // The request's fields first, all of them waited for before the partials are loaded: the partial
+  // loads sit under per-lane conditions, and with an older load still pending the compiler waits for
+  // every load issued so far after the first of them (an extra round trip).
   const ReqInfo &R = a.req[e];
-  const int local = row - R.comb_begin;
-  const int q_local = local / a.Hq, h = local - q_local * a.Hq;
-  const size_t stride = static_cast<size_t>(R.n_q) * a.Hq;  // slots between consecutive splits
-  const size_t slot0 = static_cast<size_t>(R.part_begin) + static_cast<size_t>(q_local) * a.Hq + h;
-  // every partial is loaded up front (one round trip), then merged in split order
+  const int comb_begin = R.comb_begin, n_q = R.n_q, part_begin = R.part_begin, q_begin = R.q_begin;
   const int ns = R.n_splits;
+  __builtin_amdgcn_s_waitcnt(0);
+  const int local = row - comb_begin;
+  const int q_local = local / a.Hq, h = local - q_local * a.Hq;
+  const size_t stride = static_cast<size_t>(n_q) * a.Hq;  // slots between consecutive splits
+  const size_t slot0 = static_cast<size_t>(part_begin) + static_cast<size_t>(q_local) * a.Hq + h;
+  // every partial is loaded up front (one round trip), then merged in split order
   float pm[MS], pl[MS];
   f32x4 po[MS];
 #pragma unroll
@@ -715,7 +720,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const AttnArgs a) {
     for (int k = 0; k < 4; ++k) acc[k] += wgt * po[s][k];
   }
   const float inv = 1.f / lsum;
-  const size_t orow = static_cast<size_t>(R.q_begin + q_local) * a.Hq + h;
+  const size_t orow = static_cast<size_t>(q_begin + q_local) * a.Hq + h;
   if constexpr (Cfg<T>::kBf16) {
     bf16x4 v4;
 #pragma unroll
