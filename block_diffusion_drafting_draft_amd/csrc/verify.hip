@@ -624,123 +624,192 @@ __device__ __forceinline__ double block_excl_scan(double v, double *sh, double *
   return off + wave::shift_up(incl, 0.0);
 }
 
+// Block-wide exclusive prefix sum of one double per thread with one barrier (the same arithmetic as
+// block_excl_scan); `sh` (kWaves doubles) must not be written again before the next barrier.
+__device__ __forceinline__ double block_excl_scan1(double v, double *sh, double *total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const double incl = wave::incl_scan(v, 0.0, wave::Add{});
+  if (lane == 63) sh[wv] = incl;
+  __syncthreads();
+  double off = 0.0, tot = 0.0;
+  for (int w = 0; w < kWaves; ++w) {
+    if (w < wv) off += sh[w];
+    tot += sh[w];
+  }
+  *total = tot;
+  return off + wave::shift_up(incl, 0.0);
+}
+
+// Per wavefront, the first lane with `hit` and the last lane with `pos` publish (index, value) into
+// LDS slot [wave]; after one barrier every thread takes the first hit over the wavefronts, else the
+// last positive entry. Index INT_MAX / -1: none.
+struct Pick {
+  int hit_i, last_i;
+  double hit_v, last_v;
+};
+__device__ __forceinline__ Pick block_pick(bool hit, int hit_i, double hit_v, bool pos, int last_i, double last_v,
+                                           int *sh_i, double *sh_v) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const unsigned long long hb = __ballot(hit), pb = __ballot(pos);
+  const int hl = hb ? __ffsll(static_cast<long long>(hb)) - 1 : 0;
+  const int pl = pb ? 63 - __clzll(static_cast<long long>(pb)) : 0;
+  if (lane == hl) {
+    sh_i[2 * wv] = hb ? hit_i : INT_MAX;
+    sh_v[2 * wv] = hit_v;
+  }
+  if (lane == pl) {
+    sh_i[2 * wv + 1] = pb ? last_i : -1;
+    sh_v[2 * wv + 1] = last_v;
+  }
+  __syncthreads();
+  Pick r{INT_MAX, -1, 0.0, 0.0};
+  for (int w = 0; w < kWaves; ++w) {
+    if (r.hit_i == INT_MAX && sh_i[2 * w] != INT_MAX) {
+      r.hit_i = sh_i[2 * w];
+      r.hit_v = sh_v[2 * w];
+    }
+    if (sh_i[2 * w + 1] >= 0) {
+      r.last_i = sh_i[2 * w + 1];
+      r.last_v = sh_v[2 * w + 1];
+    }
+  }
+  return r;
+}
+
 // Inside sample chunk c, whose tokens start at cumulative mass `offset`: the smallest v with
 // offset + C(v) > target. Thread t owns tokens 8t..8t+7 of the chunk; the owner is the first
 // thread whose inclusive prefix exceeds the target, and it walks its 8 masses. If rounding leaves
-// no crossing, the last token with positive mass is returned.
-struct Found {
-  int v;
-  double c_v, c_prev;
-};
-
+// no crossing, the last token with positive mass is returned. The thread that settles the token
+// writes next_token and flags (bit 1 when target is within kNear * z of the token's cumulative
+// bounds) and returns it in sh_tok (-1: no token has mass).
 template <typename T, bool VEC>
-__device__ __forceinline__ Found chunk_find(const DrawRows<T> &d, int c, int V, double offset, double target, double *sh_scan,
-                            int *sh_int, Found *sh_found) {
+__device__ __forceinline__ void chunk_find(const VerifyArgs &a, int i, const DrawRows<T> &d, int c, double offset,
+                                           double target, double z, uint32_t fl, double *sh_scan, int *sh_pi,
+                                           double *sh_pv, int *sh_tok) {
   double m[kSampleElems];
-  chunk_masses<T, VEC>(d, c, V, m);
+  chunk_masses<T, VEC>(d, c, a.vocab, m);
   double local = 0.0;
 #pragma unroll
   for (int k = 0; k < kSampleElems; ++k) local += m[k];
   double total;
-  const double start = offset + block_excl_scan(local, sh_scan, &total);
+  const double start = offset + block_excl_scan1(local, sh_scan, &total);
   const int me = static_cast<int>(threadIdx.x);
-  const int owner = block_min_int(start + local > target ? me : INT_MAX, sh_int);
-  const int last = -block_min_int(local > 0.0 ? -me : INT_MAX, sh_int);
-  if (me == 0) {
-    sh_found->v = -1;
-    sh_found->c_v = offset;
-    sh_found->c_prev = offset;
-  }
-  __syncthreads();
+  const Pick pk = block_pick(start + local > target, me, 0.0, local > 0.0, me, 0.0, sh_pi, sh_pv);
+  const int owner = pk.hit_i, last = pk.last_i;
   const bool is_owner = me == owner;
-  if (is_owner || (owner == INT_MAX && me == last)) {
+  if (is_owner || (owner == INT_MAX && me == last) || (owner == INT_MAX && last < 0 && me == 0)) {
     const int v0 = c * kSampleChunk + me * kSampleElems;
     double cum = start;
     int last_v = -1, hit_v = -1;
-    double last_c = cum, last_p = cum, hit_c = cum, hit_p = cum;
+    double last_c = offset, last_p = offset, hit_c = cum, hit_p = cum;
+    if (owner != INT_MAX || last >= 0) {
+      last_c = cum;
+      last_p = cum;
 #pragma unroll
-    for (int k = 0; k < kSampleElems; ++k) {
-      const double prev = cum;
-      cum += m[k];
-      if (m[k] > 0.0) {
-        last_v = v0 + k;
-        last_c = cum;
-        last_p = prev;
-      }
-      if (is_owner && hit_v < 0 && cum > target) {
-        hit_v = v0 + k;
-        hit_c = cum;
-        hit_p = prev;
+      for (int k = 0; k < kSampleElems; ++k) {
+        const double prev = cum;
+        cum += m[k];
+        if (m[k] > 0.0) {
+          last_v = v0 + k;
+          last_c = cum;
+          last_p = prev;
+        }
+        if (is_owner && hit_v < 0 && cum > target) {
+          hit_v = v0 + k;
+          hit_c = cum;
+          hit_p = prev;
+        }
       }
     }
     const bool h = hit_v >= 0;
-    sh_found->v = h ? hit_v : last_v;
-    sh_found->c_v = h ? hit_c : last_c;
-    sh_found->c_prev = h ? hit_p : last_p;
+    const int v = h ? hit_v : last_v;
+    const double c_v = h ? hit_c : last_c, c_prev = h ? hit_p : last_p;
+    if (fabs(target - c_v) < kNear * z || fabs(target - c_prev) < kNear * z) fl |= 2u;
+    a.next_token[i] = v;
+    if (a.flags) a.flags[i] = fl;
+    *sh_tok = v;
   }
-  __syncthreads();
-  const Found f = *sh_found;
-  __syncthreads();
-  return f;
 }
 
 // The draw of request i from its chunk masses (thread t holds chunks 4t..4t+3): chunk prefix, the
-// chunk holding u'Z, then the in-chunk scan.
+// chunk holding u'Z, then the in-chunk scan. Three barriers on the common path: the chunk prefix,
+// the choice of the chunk (first chunk whose inclusive prefix exceeds u'Z), the in-chunk prefix and
+// the choice of the owner thread (together with the chunk's, one each). Returns the token in every
+// thread when `uniform` (one more barrier).
 template <typename T, bool VEC>
 __device__ __forceinline__ int draw_token(const VerifyArgs &a, int i, const SampleState &st, DrawRows<T> d,
                                            const double (&mine)[kMaxSampleChunks / kThreads], double *sh_d,
-                                           int *sh_i, double *sh_cum, Found *sh_found) {
+                                           int *sh_i, double *sh_cum, double *sh_s1, double *sh_s2, int *sh_pi,
+                                           double *sh_pv, int *sh_pi2, double *sh_pv2, int *sh_tok, bool uniform) {
   constexpr int CPT = kMaxSampleChunks / kThreads;
   const int c0 = threadIdx.x * CPT;
   double run = 0.0;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) run += mine[k];
   double z;
-  double base = block_excl_scan(run, sh_d, &z);
+  const double base = block_excl_scan1(run, sh_s1, &z);
   z = sgpr(z);
+  uint32_t fl = st.near;
+  int c;
+  double offset, target;
+  if (z > 0.0) {
+    target = sgpr(st.u * z);
+    // this thread's chunks: the first whose inclusive prefix exceeds the target, the last with mass
+    int hit_c = INT_MAX, last_c = -1;
+    double hit_o = 0.0, last_o = 0.0, cum = base;
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    base += mine[k];
-    if (c0 + k < a.s_chunks) sh_cum[c0 + k] = base;
-  }
-  __syncthreads();
-  uint32_t fl = 0;
-  if (!(z > 0.0)) {
+    for (int k = 0; k < CPT; ++k) {
+      const double prev = cum;
+      cum += mine[k];
+      if (c0 + k < a.s_chunks) {
+        if (hit_c == INT_MAX && cum > target) {
+          hit_c = c0 + k;
+          hit_o = prev;
+        }
+        if (cum > prev) {
+          last_c = c0 + k;
+          last_o = prev;
+        }
+      }
+    }
+    const Pick pk = block_pick(hit_c != INT_MAX, hit_c, hit_o, last_c >= 0, last_c, last_o, sh_pi, sh_pv);
+    c = pk.hit_i != INT_MAX ? pk.hit_i : max(pk.last_i, 0);
+    offset = pk.hit_i != INT_MAX ? pk.hit_v : (pk.last_i >= 0 ? pk.last_v : 0.0);
+  } else {
     // zero residual mass (not reachable in exact arithmetic): draw from P instead, chunk by chunk
     fl |= 4u;
     d.mode = kBonus;
     double zp_tot = 0.0;
-    for (int c = 0; c < a.s_chunks; ++c) {
+    for (int cc = 0; cc < a.s_chunks; ++cc) {
       double m[kSampleElems];
-      chunk_masses<T, VEC>(d, c, a.vocab, m);
+      chunk_masses<T, VEC>(d, cc, a.vocab, m);
       double t = 0.0;
 #pragma unroll
       for (int k = 0; k < kSampleElems; ++k) t += m[k];
       const double cs = block_sum(t, sh_d);
-      if (threadIdx.x == 0) sh_cum[c] = zp_tot + cs;  // inclusive prefix
+      if (threadIdx.x == 0) sh_cum[cc] = zp_tot + cs;  // inclusive prefix
       zp_tot += cs;
     }
     z = zp_tot;
     __syncthreads();
+    target = sgpr(st.u * z);
+    int cand = INT_MAX, lastpos = -1;
+    for (int cc = threadIdx.x; cc < a.s_chunks; cc += kThreads) {
+      const double below = cc > 0 ? sh_cum[cc - 1] : 0.0;
+      if (cand == INT_MAX && sh_cum[cc] > target) cand = cc;
+      if (sh_cum[cc] > below) lastpos = cc;
+    }
+    const int c_star = block_min_int(cand, sh_i);
+    const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
+    c = c_star != INT_MAX ? c_star : max(c_last, 0);
+    offset = c > 0 ? sh_cum[c - 1] : 0.0;
   }
-  const double target = sgpr(st.u * z);
-  int cand = INT_MAX, lastpos = -1;
-  for (int c = threadIdx.x; c < a.s_chunks; c += kThreads) {
-    const double below = c > 0 ? sh_cum[c - 1] : 0.0;
-    if (cand == INT_MAX && sh_cum[c] > target) cand = c;
-    if (sh_cum[c] > below) lastpos = c;
-  }
-  const int c_star = block_min_int(cand, sh_i);
-  const int c_last = -block_min_int(lastpos >= 0 ? -lastpos : INT_MAX, sh_i);
-  const int c = sgpr(c_star != INT_MAX ? c_star : max(c_last, 0));
-  const double offset = sgpr(c > 0 ? sh_cum[c - 1] : 0.0);
-  const Found f = chunk_find<T, VEC>(d, c, a.vocab, offset, target, sh_d, sh_i, sh_found);
-  if (threadIdx.x == 0) {
-    if (fabs(target - f.c_v) < kNear * z || fabs(target - f.c_prev) < kNear * z) fl |= 2u;
-    a.next_token[i] = f.v;
-    if (a.flags) a.flags[i] = st.near | fl;
-  }
-  return f.v;
+  c = sgpr(c);
+  offset = sgpr(offset);
+  chunk_find<T, VEC>(a, i, d, c, offset, target, z, fl, sh_s2, sh_pi2, sh_pv2, sh_tok);
+  if (!uniform) return -1;
+  __syncthreads();
+  return *sh_tok;
 }
 
 // The slice sums of one (request, sample chunk), then, in the request's last workgroup to finish,
@@ -756,7 +825,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
   __shared__ SampleState sh_state;
   __shared__ double sh_d[kWaves * kRecFields];
   __shared__ int sh_i[kWaves];
-  __shared__ Found sh_found;
+  __shared__ double sh_s1[kWaves], sh_s2[kWaves], sh_pv[2 * kWaves], sh_pv2[2 * kWaves];
+  __shared__ int sh_pi[2 * kWaves], sh_pi2[2 * kWaves], sh_tok;
   __shared__ uint32_t sh_last;
   const int i = blockIdx.y;
   decide_request(a, i, reinterpret_cast<StatPartial *>(dyn_lds), rr, &sh_state, blockIdx.x == 0);
@@ -864,7 +934,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
         redo[k] = false;
       }
   }
-  const int tok = draw_token<T, VEC>(a, i, st, d, mine, sh_d, sh_i, reinterpret_cast<double *>(dyn_lds), &sh_found);
+  const int tok = draw_token<T, VEC>(a, i, st, d, mine, sh_d, sh_i, reinterpret_cast<double *>(dyn_lds), sh_s1, sh_s2,
+                                     sh_pi, sh_pv, sh_pi2, sh_pv2, &sh_tok, a.hit != nullptr);
   if (a.hit && threadIdx.x < 64) match_outcome(a, i, st.tgt_row - i * (a.n_draft + 1), tok);
 }
 
