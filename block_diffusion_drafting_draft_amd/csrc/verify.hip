@@ -183,10 +183,6 @@ __device__ __forceinline__ int block_min_int(int v, int *sh) {
 // |x| 2^-24 ln 2 in the term, and the terms that carry the row's mass are the ones near the top.
 // (Letting x grow to ~120 before moving, at T = 0.25 on a 151936-token row, put 3e-6 into alpha.)
 // Consumers only need some reference, not the maximum.
-// A term is one fma and one exp2: x = z c - mc with c = log2(e)/T and mc = m c rounded to fp32. The
-// fma forms z c - mc exactly before its one rounding, so x carries the same relative error as
-// (z - m) c, and the product's rounding residual rho = m c - mc (exact, by fma) is taken back out
-// at the end: the terms are relative to the reference m - rho/c, in fp64.
 struct GreedyAcc {
   float m = -INFINITY;
   int arg = INT_MAX;
@@ -209,40 +205,33 @@ struct GreedyAcc {
 };
 
 struct SumAcc {
-  float m = -INFINITY, mc = -INFINITY;
+  float m = -INFINITY;
   double s = 0.0;
 
   template <int N>
   __device__ __forceinline__ float group_sum(const float (&z)[N], float c) const {
-    float part = __builtin_amdgcn_exp2f(__builtin_fmaf(z[0], c, -mc));
+    float part = __builtin_amdgcn_exp2f((z[0] - m) * c);
 #pragma unroll
-    for (int k = 1; k < N; ++k) part += __builtin_amdgcn_exp2f(__builtin_fmaf(z[k], c, -mc));
+    for (int k = 1; k < N; ++k) part += __builtin_amdgcn_exp2f((z[k] - m) * c);
     return part;
   }
 
-  // With no finite logit seen yet mc = -inf, and a group holding one makes the sum +inf or NaN, so
-  // the one test below also sets the first reference.
+  // With no finite logit seen yet m = -inf, and a group holding one makes the sum +inf or NaN, so
+  // the one test below also sets the first reference. (The argument is formed as (z - m) * c rather
+  // than z * c - m * c: with m * c the reference itself would overflow fp32 at tiny temperatures.)
   template <int N>
-  __device__ __forceinline__ void fold(const float (&z)[N], int, float c, double) {
+  __device__ __forceinline__ void fold(const float (&z)[N], int, float c, double inv_t) {
     float part = group_sum(z, c);
     if (!(part < 0x1p8f)) {
       float vm = z[0];
 #pragma unroll
       for (int k = 1; k < N; ++k) vm = fmaxf(vm, z[k]);
       if (vm == -INFINITY) return;  // no finite logit in the group, none before it either
-      const float nmc = vm * c;
-      s = m == -INFINITY ? 0.0 : s * exp_fp64((static_cast<double>(mc) - nmc) * 0.6931471805599453);
+      s = m == -INFINITY ? 0.0 : s * exp_fp64((static_cast<double>(m) - vm) * inv_t);
       m = vm;
-      mc = nmc;
       part = group_sum(z, c);
     }
     s += static_cast<double>(part);
-  }
-
-  // the reference the terms are taken against, in logit units (only when m is finite)
-  __device__ __forceinline__ double ref(float c) const {
-    const float rho = __builtin_fmaf(m, c, -mc);
-    return static_cast<double>(m) - static_cast<double>(rho) / static_cast<double>(c);
   }
 };
 
@@ -331,7 +320,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
     out.aux = block_min_int(acc.m == m ? acc.arg : INT_MAX, sh_i);
     out.sum = 0.0;
   } else {
-    const double mine = acc.m == -INFINITY ? 0.0 : acc.s * exp_fp64((acc.ref(a.c_log2) - m) * a.inv_t);
+    const double mine =
+        acc.m == -INFINITY ? 0.0 : acc.s * exp_fp64((static_cast<double>(acc.m) - m) * a.inv_t);
     out.sum = block_sum(mine, sh_d);
     out.aux = has_y ? __float_as_int(zy) : 0;
   }
