@@ -144,7 +144,8 @@ FUZZ = [
     ("bf16", 5, 24, 32000, 1.0, "zipf"),
     ("f32", 3, 16, 1, 1.0, "iid"),        # one-token vocabulary: everything accepted
     ("bf16", 2, 8, 5000, 0.05, "zipf"),   # low temperature: scaled logits span hundreds
-    ("bf16", 2, 8, 5000, 1e-30, "zipf"),  # tiny temperature: logit * log2(e)/T is beyond fp32's range
+    # tiny temperature: every row's top logit times log2(e)/T (1.2e38) is beyond fp32's range
+    ("bf16", 2, 8, 5000, 1.2e-38, "zipf"),
     ("f32", 2, 8, 3000, 0.02, "iid"),
     ("bf16", 2, 16, 151936, 0.0, "zipf"),  # greedy
     ("f32", 6, 8, 50, 0.0, "iid"),        # greedy, small
