@@ -50,7 +50,8 @@ def parse():
                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                         "dispatch that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--no-serve-verify", action="store_true",
-                   help="skip the serving batch's verify measurement (warm and cold)")
+                   help="skip the serving batch's verify measurement (warm and cold) and the synchronous "
+                        "draft's attention call")
     p.add_argument("--no-next-rows", action="store_true",
                    help="skip the next-row measurements (token selection, KV commit, AWL, training attention)")
     p.add_argument("--call", choices=("round", "descriptor_build_device", "draft_attn_packed", "spec_verify",
@@ -419,6 +420,7 @@ def main():
     t_ver_cold = summary(verify_cold_us(r.lib, r.z_t, r.z_d, r.tokens, r.vin["temperature"], r.vin["philox_seed"],
                                         r.round, r.ver_ws, r.ver_out, per_replay_us, reps))
     serve = None if args.no_serve_verify else verify_serve(torch, mean_us, per_replay_us, summary, reps)
+    sync = sync_attention(torch, mean_us, reps) if w.coverage and not args.no_serve_verify else None
     # the host path for comparison: CPU time of the batched host builder, and the copy of its batch
     scratch = torch.empty_like(r.desc_host)
     n_host = 2000
@@ -499,6 +501,8 @@ def main():
     }
     if serve is not None:
         out["verify_serve"] = serve
+    if sync is not None:
+        out["sync_attention"] = sync
     if not args.no_next_rows:
         out["next_rows"] = {"draft_topk": next_row_topk(r, torch, cur, mean_us),
                             "kv_commit": next_row_commit(r, torch, mean_us),
@@ -531,6 +535,33 @@ def verify_cold_us(lib, zt, zd, tokens, temperature, seed, round_, ws, out, per_
         cold.append(per_replay_us(graphs[k % 3], 1, warmup=0)[0])
     del flush, sink, copies, graphs
     return np.array(cold)
+
+
+def sync_attention(torch, mean_us, reps):
+    """draft_attn_packed of the synchronous draft a cache miss falls back to (one request, one
+    16-query block, 32/8 heads, d = 128, 2048-token prefix): device time per call in a graph of 10
+    back-to-back copies, and per replay of a one-call graph."""
+    from block_diffusion_drafting_draft_amd import synth
+    w = synth.WORKLOADS["sync-bf16-L2048-V151936"]
+    r = Round(w)
+    r.build_descs()
+    for _ in range(3):
+        r.attention()
+    torch.cuda.synchronize()
+    g1, g10 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        r.attention()
+    with torch.cuda.graph(g10):
+        for _ in range(10):
+            r.attention()
+    torch.cuda.synchronize()
+    t1 = mean_us(g1, reps)
+    t10 = mean_us(g10, 30) / 10
+    flops = r.work()[0]
+    del g1, g10, r
+    return {"workload": w.name, "us_in_graph": round(t10, 3), "us_single_replay": round(t1, 3),
+            "tflops_in_graph": round(flops / (t10 * 1e-6) / 1e12, 2),
+            "pct_mfma_peak_in_graph": round(100 * flops / (t10 * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2)}
 
 
 def verify_serve(torch, mean_us, per_replay_us, summary, reps):
