@@ -249,8 +249,8 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: every box here has a single GPU, so --gpus {args.gpus} is not run "
-              f"(the path shards by request or key/value head; see the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the path is built and measured on a single GPU, so --gpus {args.gpus} "
+              f"is not run (it would shard by request or key/value head).", file=sys.stderr)
         return 2
     import torch
     from block_diffusion_drafting_draft_amd import synth

@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly (not skip) when the HIP library is missing on a GPU machine; on a host
+    # GPU tests fail loudly (not skip) when the HIP library is missing on a machine with a GPU; on a host
     # without a GPU they are only deselected by -m "not gpu".
     pass
 
