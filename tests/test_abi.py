@@ -141,6 +141,13 @@ def test_workspace_sizes():
     assert _binding.draft_attn_packed_workspace("bf16", [0, 24], [4096], 16, 32, 8, 96) == 0
     assert _binding.spec_verify_workspace(16, 15, 151936) > 0
     assert _binding.spec_verify_workspace(1, 64, 10) == 0
+    # statistics partials (16 B per row and chunk), sample records (40 B per request and 2048-token
+    # chunk), per-request counters (256 B apart), each region 256-aligned. The statistics grid stays
+    # within 1024 workgroups: 2 chunks per row for the serving batch's 496 rows, the cap of 8 for one
+    # request's 31 rows.
+    align = lambda x: (x + 255) // 256 * 256
+    assert _binding.spec_verify_workspace(16, 15, 151936) == align(16 * 496 * 2) + align(40 * 16 * 75) + 16 * 256
+    assert _binding.spec_verify_workspace(1, 15, 151936) == align(16 * 31 * 8) + align(40 * 75) + 256
 
 
 def test_topk_workspace():
