@@ -514,6 +514,43 @@ __device__ __forceinline__ void load8(const T *row, int v0, int V, float (&z)[kS
   }
 }
 
+// 2^(j/32), j = 0..31, rounded to fp64 (computed to 60 digits and rounded once).
+__device__ constexpr double kExp2Frac[32] = {
+    0x1.0000000000000p+0, 0x1.059b0d3158574p+0, 0x1.0b5586cf9890fp+0, 0x1.11301d0125b51p+0,
+    0x1.172b83c7d517bp+0, 0x1.1d4873168b9aap+0, 0x1.2387a6e756238p+0, 0x1.29e9df51fdee1p+0,
+    0x1.306fe0a31b715p+0, 0x1.371a7373aa9cbp+0, 0x1.3dea64c123422p+0, 0x1.44e086061892dp+0,
+    0x1.4bfdad5362a27p+0, 0x1.5342b569d4f82p+0, 0x1.5ab07dd485429p+0, 0x1.6247eb03a5585p+0,
+    0x1.6a09e667f3bcdp+0, 0x1.71f75e8ec5f74p+0, 0x1.7a11473eb0187p+0, 0x1.82589994cce13p+0,
+    0x1.8ace5422aa0dbp+0, 0x1.93737b0cdc5e5p+0, 0x1.9c49182a3f090p+0, 0x1.a5503b23e255dp+0,
+    0x1.ae89f995ad3adp+0, 0x1.b7f76f2fb5e47p+0, 0x1.c199bdd85529cp+0, 0x1.cb720dcef9069p+0,
+    0x1.d5818dcfba487p+0, 0x1.dfc97337b9b5fp+0, 0x1.ea4afa2a490dap+0, 0x1.f50765b6e4540p+0,
+};
+
+// exp(x) in fp64, table-driven (P. T. P. Tang, "Table-driven implementation of the exponential function
+// in IEEE floating-point arithmetic", ACM TOMS 15(2), 1989): x = (32 k + j) ln2/32 + r with |r| <= ln2/64
+// (Cody-Waite: ln2/32 split into a head whose products with the integer are exact and a tail), e^r by
+// its Taylor series to degree 6 (truncation below 2e-18 relative), times 2^(j/32) from `tab` (the table
+// above, staged in LDS) and 2^k. About 12 fp64 operations and one LDS read against exp_fp64's 18. NaN and
+// arguments below the smallest subnormal give 0.
+__device__ __forceinline__ double exp_fp64_tab(double x, const double *tab) {
+  constexpr double kInvStep = 46.16624130844683;      // 32 / ln 2
+  constexpr double kStepHi = 0.021660834550857544;    // (ln 2 with its low 32 mantissa bits cleared) / 32
+  constexpr double kStepLo = 1.4841640746973977e-08;  // ln 2 / 32 - kStepHi
+  if (!(x > -745.5)) return 0.0;
+  const double n = rint(x * kInvStep);
+  double r = fma(-n, kStepHi, x);
+  r = fma(-n, kStepLo, r);
+  double p = 1.0 / 720.0;
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ni = static_cast<int>(n);
+  return ldexp(p * tab[ni & 31], ni >> 5);
+}
+
 template <typename T>
 struct DrawRows {
   const T *p;
@@ -521,14 +558,15 @@ struct DrawRows {
   float mp, mq;
   double inv_t, log_sp, log_sq;
   int mode;
+  const double *tab;  // kExp2Frac in LDS
   // Mass of a token with target logit zp and draft logit zq in the law being drawn from:
   // max(0, P - Q) after a rejection, P for the bonus draw or the zero-mass fallback.
   __device__ __forceinline__ double mass(float zp, float zq) const {
     const double ap = (static_cast<double>(zp) - mp) * inv_t - log_sp;
-    if (mode != kResidual) return exp_fp64(ap);
+    if (mode != kResidual) return exp_fp64_tab(ap, tab);
     const double aq = (static_cast<double>(zq) - mq) * inv_t - log_sq;
     if (!(ap > aq)) return 0.0;  // P(v) <= Q(v): no residual mass, no exp needed
-    return fmax(0.0, exp_fp64(ap) - exp_fp64(aq));
+    return fmax(0.0, exp_fp64_tab(ap, tab) - exp_fp64_tab(aq, tab));
   }
 };
 
@@ -819,11 +857,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
   __shared__ int sh_pi[2 * kWaves], sh_pi2[2 * kWaves], sh_tok;
   __shared__ uint32_t sh_last;
   const int i = blockIdx.y;
+  __shared__ double sh_exp2[32];
+  if (threadIdx.x < 32) sh_exp2[threadIdx.x] = kExp2Frac[threadIdx.x];
   decide_request(a, i, reinterpret_cast<StatPartial *>(dyn_lds), rr, &sh_state, blockIdx.x == 0);
   __syncthreads();
   const SampleState st = uniform_state(sh_state);  // in scalar registers: the budget is 80 VGPRs
   if (st.mode == kDone) return;
   DrawRows<T> d = draw_rows_base<T>(a, st);
+  d.tab = sh_exp2;
   const bool residual = st.mode == kResidual;
   {
     const int v0 = blockIdx.x * kSampleChunk + static_cast<int>(threadIdx.x) * kSampleElems;
@@ -836,11 +877,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
 #pragma unroll
     for (int k = 0; k < kSampleElems; ++k) {
       const double ap = (static_cast<double>(zp[k]) - ref_p) * a.inv_t;
-      const double ep = exp_fp64(ap);
+      const double ep = exp_fp64_tab(ap, sh_exp2);
       s[0] += ep;
       if (residual) {
         const double aq = (static_cast<double>(zq[k]) - ref_q) * a.inv_t;
-        const double eq = exp_fp64(aq);
+        const double eq = exp_fp64_tab(aq, sh_exp2);
         s[1] += eq;
         if (ep > 0.0) {  // a token without target mass has no residual mass
           const double t = (ap - aq) - st.rho;
