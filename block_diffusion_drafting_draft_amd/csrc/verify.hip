@@ -54,6 +54,9 @@ constexpr int kWaves = kThreads / 64;
 // row) every workgroup starts within 1 us, and the call measured 70.6 -> 68.1 us cold, 62.7 -> 61.7
 // warm (1488 workgroups: 69.4 / 60.8).
 constexpr int kStatSlots = 1024;
+// Threads per statistics workgroup: 512 against 256 took the async verify from 21.0 to 20.2 us
+// in-graph (twice the threads per chunk of its 248 workgroups); the serving batch did not move.
+constexpr int kStatThreads = 512;
 constexpr int kStatMinChunk = 1024;
 // Per row: more chunks only lengthen decide's staging and row merge. At a single request's 31 rows
 // (the async round) 8 chunks measured ~1 us faster in the round than 32, and no slower alone.
@@ -138,35 +141,38 @@ __device__ __forceinline__ void match_outcome(const VerifyArgs &a, int i, int n_
 // ------------------------------------------------------------------------------------------------
 // block reductions (256 threads = 4 wavefronts)
 // ------------------------------------------------------------------------------------------------
+template <int NW = kWaves>
 __device__ __forceinline__ float block_max(float v, float *sh) {
   v = wave::reduce(v, 64, wave::Max{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
   __syncthreads();
   float r = sh[0];
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
+  for (int i = 1; i < NW; ++i) r = fmaxf(r, sh[i]);
   __syncthreads();
   return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ double block_sum(double v, double *sh) {
   v = wave::reduce(v, 64, wave::Add{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
   __syncthreads();
   double r = sh[0];
-  for (int i = 1; i < kWaves; ++i) r += sh[i];
+  for (int i = 1; i < NW; ++i) r += sh[i];
   __syncthreads();
   return r;
 }
 
+template <int NW = kWaves>
 __device__ __forceinline__ int block_min_int(int v, int *sh) {
   v = wave::reduce(v, 64, wave::Min{});
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
   __syncthreads();
   int r = sh[0];
-  for (int i = 1; i < kWaves; ++i) r = min(r, sh[i]);
+  for (int i = 1; i < NW; ++i) r = min(r, sh[i]);
   __syncthreads();
   return r;
 }
@@ -266,10 +272,11 @@ __device__ __forceinline__ int row_token(const VerifyArgs &a, int row) {
 }
 
 template <typename T, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
-  __shared__ float sh_f[kWaves];
-  __shared__ double sh_d[kWaves];
-  __shared__ int sh_i[kWaves];
+__global__ __launch_bounds__(kStatThreads) void stats_kernel(const VerifyArgs a) {
+  constexpr int NW = kStatThreads / 64;
+  __shared__ float sh_f[NW];
+  __shared__ double sh_d[NW];
+  __shared__ int sh_i[NW];
   const int row = blockIdx.y;
   const int chunk = blockIdx.x;
   const T *base = row < a.n_tgt_rows
@@ -291,38 +298,38 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(const VerifyArgs a) {
     constexpr int U = 4;
     // steps of U vectors per thread with every load in range (no per-load test), then the rest
     int v = threadIdx.x;
-    for (; v + (U - 1) * kThreads < nvec; v += U * kThreads) {
+    for (; v + (U - 1) * kStatThreads < nvec; v += U * kStatThreads) {
       u32x4 buf[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) buf[u] = vp[v + u * kThreads];
+      for (int u = 0; u < U; ++u) buf[u] = vp[v + u * kStatThreads];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         float z[W];
         unpack(buf[u], z, static_cast<const T *>(nullptr));
-        acc.fold(z, begin + (v + u * kThreads) * W, a.c_log2, a.inv_t);
+        acc.fold(z, begin + (v + u * kStatThreads) * W, a.c_log2, a.inv_t);
       }
     }
-    for (; v < nvec; v += kThreads) {
+    for (; v < nvec; v += kStatThreads) {
       float z[W];
       unpack(vp[v], z, static_cast<const T *>(nullptr));
       acc.fold(z, begin + v * W, a.c_log2, a.inv_t);
     }
   } else {
-    for (int idx = begin + threadIdx.x; idx < end; idx += kThreads) {
+    for (int idx = begin + threadIdx.x; idx < end; idx += kStatThreads) {
       float z[1] = {load_elem(base + idx)};
       acc.fold(z, idx, a.c_log2, a.inv_t);
     }
   }
-  const float m = block_max(acc.m, sh_f);
+  const float m = block_max<NW>(acc.m, sh_f);
   StatPartial out;
   out.max = m;
   if constexpr (GREEDY) {
-    out.aux = block_min_int(acc.m == m ? acc.arg : INT_MAX, sh_i);
+    out.aux = block_min_int<NW>(acc.m == m ? acc.arg : INT_MAX, sh_i);
     out.sum = 0.0;
   } else {
     const double mine =
         acc.m == -INFINITY ? 0.0 : acc.s * exp_fp64((static_cast<double>(acc.m) - m) * a.inv_t);
-    out.sum = block_sum(mine, sh_d);
+    out.sum = block_sum<NW>(mine, sh_d);
     out.aux = has_y ? __float_as_int(zy) : 0;
   }
   if (threadIdx.x == 0) {
@@ -1013,9 +1020,9 @@ int launch_verify(const VerifyArgs &a, hipStream_t stream) {
   const int stat_rows = a.greedy ? a.n_tgt_rows : a.n_req * (2 * a.n_draft + 1);
   const dim3 stat_grid(a.chunks, stat_rows);
   if (a.greedy)
-    stats_kernel<T, VEC, true><<<stat_grid, kThreads, 0, stream>>>(a);
+    stats_kernel<T, VEC, true><<<stat_grid, kStatThreads, 0, stream>>>(a);
   else
-    stats_kernel<T, VEC, false><<<stat_grid, kThreads, 0, stream>>>(a);
+    stats_kernel<T, VEC, false><<<stat_grid, kStatThreads, 0, stream>>>(a);
   const int rows_req = a.greedy ? a.n_draft + 1 : 2 * a.n_draft + 1;
   // the dynamic stage holds decide's partials, then (last workgroup) the pick's chunk prefix
   const size_t lds = std::max(sizeof(StatPartial) * static_cast<size_t>(rows_req) * a.chunks,
